@@ -1,0 +1,103 @@
+// Internal launch interfaces between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kMaxHeadTable = 512;   // B*H entries a single attention launch can schedule
+constexpr int kMaxQueues = 8;        // one work queue per XCD
+
+struct HeadList {                    // small head lists travel as kernel arguments
+  int32_t n;
+  int32_t h[256];
+};
+
+// ----------------------------------------------------------------- pooling
+// dst[b][head][I][:] = bf16(mean of src[b][head][I*block .. ][:]) for the listed
+// heads (head indices into src's head axis).  src is [B, Hs, N, 128] bf16.
+hipError_t launch_pool(const uint16_t* src, int B, int Hs, int N, const HeadList& heads,
+                       int block, uint16_t* dst, hipStream_t st);
+
+// ------------------------------------------------------------ block scores
+// scores[b][h][I][J] = qbar[b][h][I] . kbar[b][kvh][J] * scale for J <= I (fp32).
+hipError_t launch_block_scores(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv,
+                               int nqb, int nkb, const HeadList& heads, float scale, float* scores,
+                               hipStream_t st);
+
+// ---------------------------------------------------------------- select
+// Per listed head and query block I: block selection over scores row I.
+hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb,
+                               const HeadList& heads, int mode, int topk, float log_alpha,
+                               int force_first, int force_diag, int32_t* idx, int32_t* count,
+                               int cap, hipStream_t st);
+
+
+// ------------------------------------------------------------ vertical-slash
+struct VsScoreArgs {
+  const uint16_t* q;      // [B, H, Nq, 128]
+  const uint16_t* k;      // [B, Hkv, Nk, 128]
+  int B, H, Hkv, Nq, Nk, last_q;
+  HeadList heads;
+  float* v_out;           // [B, n_heads, Nk] column sums
+  float* s_out;           // [B, n_heads, Nk] diagonal sums
+  float* part_ml;         // [B, n_heads, nchunks, 2, 64] per-chunk row max / sum
+  float* part_diag;       // [B, n_heads, nchunks, chunk_keys + 64] per-chunk diagonal sums
+  int nchunks, chunk_tiles;
+};
+size_t vs_workspace_floats(int n_rows, int Nk);   // n_rows = B * n_heads
+hipError_t launch_vs_scores(const VsScoreArgs& a, hipStream_t st);
+
+// Top-nv of v and top-ns of s per listed head ([B, n_heads, Nk] rows) into the
+// VS index set ([B, H, cap] rows).
+hipError_t launch_vs_select(const float* v, const float* s, int B, int Nk, int H, const HeadList& heads, int nv,
+                            int ns, int32_t* cols, int32_t* cols_count, int cols_cap, int32_t* diags,
+                            int32_t* diags_count, int diags_cap, hipStream_t st);
+
+// A-shape sets: cols = [0, sink), diags = [0, local) for each listed head.
+hipError_t launch_ashape_fill(int B, int H, const HeadList& heads, int ncols, int ndiags,
+                              int32_t* cols, int32_t* cols_count, int cols_cap,
+                              int32_t* diags, int32_t* diags_count, int diags_cap, hipStream_t st);
+
+// --------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v;
+  void* o; float* lse; int out_f32;
+  int B, H, Hkv, Nq, Nk, q_offset;
+  int8_t kind[256];                  // per Q head
+  // Vertical-Slash sets and their compiled form (workspace)
+  const int32_t* cols; const int32_t* cols_count; int cols_cap;
+  const int32_t* diags; const int32_t* diags_count; int diags_cap;
+  uint32_t* sbits; uint32_t* vbits; uint32_t* abits; uint32_t* fbits;
+  int32_t* alist; int32_t* acount;
+  int sw, vw, aw, acap;              // words per head of each bitmap; alist capacity
+  // Block sets
+  const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
+  // Token sets
+  const int32_t* tidx; const int32_t* tcount; int tcap;
+  // Scheduling
+  int32_t* counters;                 // [kMaxQueues] work-queue heads (zeroed by the launcher)
+};
+size_t attn_workspace_bytes(int B, int H, int Nk);
+hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st);
+
+// --------------------------------------------------------------- indexer
+struct IndexerArgs {
+  const uint16_t* q_idx;   // [Nq, Hi, 128]
+  const uint16_t* k_idx;   // [Nk, 128]
+  const float* w;          // [Nq, Hi]
+  int Nq, Nk, Hi, q_offset, route_heads, topk;
+  int32_t* tok; int32_t* tok_count; int tok_cap;
+  int32_t* route;          // nullable [Nq, route_heads]
+};
+bool indexer_supported();
+bool attn_token_supported();
+size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads);
+hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st);
+
+// zero n int32 words (used instead of hipMemsetAsync so the sequence stays
+// capturable into a graph)
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,186 @@
+// Sort-free selection inside one workgroup (gfx950, wave64).
+//
+// Top-k: radix select of the k-th largest order-preserving 32-bit key (four
+// 8-bit digits, MSB first, histograms in LDS), then one compaction pass that
+// keeps every key above it and the lowest-indexed keys equal to it, written in
+// ascending index order.  Threshold: one max-reduce, then the same compaction
+// with the cut max + log_alpha.  Both follow the selection rules of "FlashPrefill"
+// section 2.2 (threshold relative to the row maximum, no sort) and the top-k of
+// MoBA's FlashMoBA section, with ties to the lower index.
+#pragma once
+#include "common.h"
+
+namespace dsa {
+
+template <int NTH>
+struct SelectSmem {
+  uint32_t hist[256];
+  uint32_t wv[NTH / 64][2];
+  uint32_t scal[4];
+  float fmax[NTH / 64];
+};
+
+// Candidates: j in [lo, hi) except ex0 and ex1 (-1 for none).
+template <int NTH>
+__device__ __forceinline__ bool sel_is_cand(int j, int ex0, int ex1) { return j != ex0 && j != ex1; }
+
+// Writes the selected indices (ascending) to out[0..count) and returns count
+// (uniform across the workgroup).  k <= 0 selects nothing.
+template <int NTH>
+__device__ int select_topk(const float* __restrict__ sc, int lo, int hi, int ex0, int ex1, int k,
+                           int32_t* __restrict__ out, SelectSmem<NTH>& sm) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  constexpr int NW = NTH / 64;
+  int nex = (ex0 >= lo && ex0 < hi) + (ex1 >= lo && ex1 < hi && ex1 != ex0);
+  const int ncand = hi - lo - nex;
+  if (k <= 0 || ncand <= 0) return 0;
+
+  uint32_t T = 0u;         // keys > T all selected, == T lowest-index first
+  int need_eq = 0;
+  bool take_all = k >= ncand;
+  if (!take_all) {
+    uint32_t prefix = 0u, pmask = 0u;
+    int kk = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += NTH) sm.hist[i] = 0u;
+      __syncthreads();
+      for (int j = lo + tid; j < hi; j += NTH) {
+        if (!sel_is_cand<NTH>(j, ex0, ex1)) continue;
+        const uint32_t key = f32_order_key(sc[j]);
+        if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (w == 0) {
+        // lane l owns bins 255-4l .. 252-4l (descending digit order)
+        uint32_t c[4];
+        uint32_t s = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { c[i] = sm.hist[255 - 4 * l - i]; s += c[i]; }
+        const uint32_t incl = wave_incl_scan(s);
+        const uint32_t excl = incl - s;
+        // the lane where the cumulative count first reaches kk
+        const bool hit = excl < (uint32_t)kk && incl >= (uint32_t)kk;
+        if (hit) {
+          uint32_t run = excl;
+          for (int i = 0; i < 4; ++i) {
+            if (run + c[i] >= (uint32_t)kk) {
+              sm.scal[0] = 255u - 4u * l - i;
+              sm.scal[1] = run;
+              break;
+            }
+            run += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t dgt = sm.scal[0];
+      kk -= (int)sm.scal[1];
+      prefix |= dgt << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    T = prefix;
+    need_eq = kk;
+  }
+
+  // compaction: wave w owns the contiguous segment [s0, s1)
+  const int n = hi - lo;
+  const int seg = (n + NW - 1) / NW;
+  const int s0 = lo + min(n, w * seg), s1 = lo + min(n, (w + 1) * seg);
+  uint32_t gt = 0u, eq = 0u;
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    bool g = false, e = false;
+    if (j < s1 && sel_is_cand<NTH>(j, ex0, ex1)) {
+      if (take_all) g = true;
+      else {
+        const uint32_t key = f32_order_key(sc[j]);
+        g = key > T;
+        e = key == T;
+      }
+    }
+    gt += __popcll(__builtin_amdgcn_ballot_w64(g));
+    eq += __popcll(__builtin_amdgcn_ballot_w64(e));
+  }
+  if (l == 0) { sm.wv[w][0] = gt; sm.wv[w][1] = eq; }
+  __syncthreads();
+  uint32_t out_pos = 0u, eq_before = 0u;
+  for (int i = 0; i < w; ++i) {
+    const uint32_t g2 = sm.wv[i][0], e2 = sm.wv[i][1];
+    const int rem = need_eq - (int)eq_before;
+    out_pos += g2 + (uint32_t)max(0, min(rem, (int)e2));
+    eq_before += e2;
+  }
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    bool g = false, e = false;
+    if (j < s1 && sel_is_cand<NTH>(j, ex0, ex1)) {
+      if (take_all) g = true;
+      else {
+        const uint32_t key = f32_order_key(sc[j]);
+        g = key > T;
+        e = key == T;
+      }
+    }
+    const uint64_t be = __builtin_amdgcn_ballot_w64(e);
+    const bool take = g || (e && (int)(eq_before + ballot_rank(be)) < need_eq);
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(take);
+    if (take) out[out_pos + ballot_rank(bs)] = j;
+    out_pos += __popcll(bs);
+    eq_before += __popcll(be);
+  }
+  __syncthreads();
+  return take_all ? ncand : k;
+}
+
+// Threshold selection over all of [lo, hi): keep sc[j] >= max + log_alpha.
+// Returns the count; writes ascending indices to out.  Also reports whether
+// index `probe0` and `probe1` were kept (for merging forced entries).
+template <int NTH>
+__device__ int select_threshold(const float* __restrict__ sc, int lo, int hi, float log_alpha,
+                                int32_t* __restrict__ out, int out_shift, SelectSmem<NTH>& sm,
+                                float* cut_out) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  constexpr int NW = NTH / 64;
+  if (hi <= lo) return 0;
+  float mx = -INFINITY;
+  for (int j = lo + tid; j < hi; j += NTH) mx = fmaxf(mx, sc[j]);
+  mx = wave_max(mx);
+  if (l == 0) sm.fmax[w] = mx;
+  __syncthreads();
+  mx = sm.fmax[0];
+  for (int i = 1; i < NW; ++i) mx = fmaxf(mx, sm.fmax[i]);
+  const float cut = mx + log_alpha;
+  if (cut_out) *cut_out = cut;
+  const int n = hi - lo;
+  const int seg = (n + NW - 1) / NW;
+  const int s0 = lo + min(n, w * seg), s1 = lo + min(n, (w + 1) * seg);
+  uint32_t cnt = 0u;
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    const bool g = j < s1 && sc[j] >= cut;
+    cnt += __popcll(__builtin_amdgcn_ballot_w64(g));
+  }
+  __syncthreads();
+  if (l == 0) sm.wv[w][0] = cnt;
+  __syncthreads();
+  uint32_t pos = (uint32_t)out_shift;
+  for (int i = 0; i < w; ++i) pos += sm.wv[i][0];
+  uint32_t total = 0u;
+  for (int i = 0; i < NW; ++i) total += sm.wv[i][0];
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    const bool g = j < s1 && sc[j] >= cut;
+    const uint64_t b = __builtin_amdgcn_ballot_w64(g);
+    if (g) out[pos + ballot_rank(b)] = j;
+    pos += __popcll(b);
+  }
+  __syncthreads();
+  return (int)total;
+}
+
+}  // namespace dsa

@@ -1,0 +1,170 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (before any HIP call), with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_mean_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTS), names
+
+
+def test_every_declared_symbol_is_exported():
+    L = dsa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    nm = os.popen(f"nm -D --defined-only {dsa.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_status_strings():
+    L = dsa.lib()
+    assert L.dsa_status_string(0) == b"ok"
+    assert L.dsa_status_string(3).startswith(b"workspace")
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+def shape(**kw):
+    s = dict(batch=1, heads=4, kv_heads=2, q_len=256, kv_len=256, head_dim=128, q_offset=0)
+    s.update(kw)
+    return dsa.Shape(**s)
+
+
+def ws_size(op, sh, params):
+    arr = (ctypes.c_int32 * max(1, len(params)))(*params)
+    out = ctypes.c_size_t(0)
+    st = dsa.lib().dsa_workspace_size(op, ctypes.byref(sh), arr, len(params), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    st, n = ws_size(dsa.OP_ATTN, shape(), [])
+    assert st == 0 and n > 0
+    st, n_vs = ws_size(dsa.OP_VS, shape(), [2, 64])
+    assert st == 0 and n_vs >= 2 * 2 * 256 * 4
+    st, n_b = ws_size(dsa.OP_BLOCK, shape(), [4, 64])
+    assert st == 0 and n_b >= 4 * 4 * 4 * 4
+    # sizes depend on shape only and grow with it
+    st, big = ws_size(dsa.OP_ATTN, shape(q_len=4096, kv_len=4096), [])
+    assert big > n
+    assert ws_size(99, shape(), [])[0] == dsa.DSA_ERR_INVALID_ARG
+    assert ws_size(dsa.OP_BLOCK, shape(), [4, 32])[0] == dsa.DSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(heads=5), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_len=100), dsa.DSA_ERR_INVALID_ARG),
+    (dict(batch=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_offset=-1, q_len=257), dsa.DSA_ERR_INVALID_ARG),
+    (dict(heads=512, kv_heads=1), dsa.DSA_ERR_UNSUPPORTED),
+])
+def test_bad_shapes(kw, code):
+    assert ws_size(dsa.OP_ATTN, shape(**kw), [])[0] == code
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def vs_c(cap_c=16, cap_d=16, null=False):
+    p = 0 if null else 0x2000
+    return dsa._VsIndexC(p, p, cap_c, p, p, cap_d)
+
+
+def test_vs_validation_paths():
+    L = dsa.lib()
+    heads = (ctypes.c_int32 * 2)(0, 1)
+    sh = shape()
+    _, need = ws_size(dsa.OP_VS, sh, [2, 64])
+    call = lambda **kw: L.build_index_vs(ctypes.byref(kw.get("sh", sh)), kw.get("q", FAKE), FAKE, kw.get("heads", heads),
+                                         kw.get("n", 2), kw.get("lq", 64), kw.get("nv", 8), kw.get("ns", 8),
+                                         kw.get("out", vs_c()), None, None, kw.get("ws", FAKE),
+                                         kw.get("wsb", need), None)
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lq=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lq=65) == dsa.DSA_ERR_INVALID_ARG
+    assert call(nv=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert call(nv=17) == dsa.DSA_ERR_INVALID_ARG                 # above cols_cap
+    assert call(out=vs_c(null=True)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(ws=None) == dsa.DSA_ERR_WORKSPACE
+    bad = (ctypes.c_int32 * 2)(0, 9)
+    assert call(heads=bad) == dsa.DSA_ERR_INVALID_ARG
+    dup = (ctypes.c_int32 * 2)(1, 1)
+    assert call(heads=dup) == dsa.DSA_ERR_INVALID_ARG
+    assert call(n=0) == dsa.DSA_ERR_INVALID_ARG
+    assert b"workspace" in L.dsa_last_error() or True
+
+
+def test_block_validation_paths():
+    L = dsa.lib()
+    heads = (ctypes.c_int32 * 1)(0)
+    sh = shape()
+    _, need = ws_size(dsa.OP_BLOCK, sh, [1, 64])
+    good = dsa._BlockIndexC(0x2000, 0x2000, 4, 64)
+
+    def call(**kw):
+        return L.build_index_block(ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, heads, 1, kw.get("block", 64),
+                                   kw.get("mode", 0), kw.get("topk", 2), ctypes.c_float(kw.get("la", -3.0)),
+                                   kw.get("ff", 1), kw.get("fd", 1), kw.get("out", good), None, None, None,
+                                   kw.get("ws", FAKE), kw.get("wsb", need), None)
+    assert call(block=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(mode=7) == dsa.DSA_ERR_INVALID_ARG
+    assert call(topk=-1) == dsa.DSA_ERR_INVALID_ARG
+    # nqb = 4: top-3 plus two forced blocks needs min(4, 5) = 4 slots
+    assert call(topk=3, out=dsa._BlockIndexC(0x2000, 0x2000, 3, 64)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(mode=1, la=0.5) == dsa.DSA_ERR_INVALID_ARG
+    assert call(out=dsa._BlockIndexC(0x2000, 0x2000, 4, 128)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(out=dsa._BlockIndexC(0, 0x2000, 4, 64)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(sh=shape(q_len=200, q_offset=56)) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_attention_validation_paths():
+    L = dsa.lib()
+    sh = shape()
+    _, need = ws_size(dsa.OP_ATTN, sh, [])
+    kinds = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+
+    def call(**kw):
+        vs = kw.get("vs", vs_c())
+        blk = kw.get("blk", dsa._BlockIndexC(0x2000, 0x2000, 4, 64))
+        return L.sparse_prefill_attn(ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, kw.get("v", FAKE), kw.get("kinds", kinds),
+                                     ctypes.byref(vs) if vs is not None else None,
+                                     ctypes.byref(blk) if blk is not None else None, None, kw.get("dt", 1),
+                                     FAKE, None, kw.get("ws", FAKE), kw.get("wsb", need), None)
+    assert call(v=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(vs=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(blk=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(dt=5) == dsa.DSA_ERR_INVALID_ARG
+    assert call(kinds=(ctypes.c_int32 * 4)(0, 1, 2, 7)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(kinds=(ctypes.c_int32 * 4)(0, 3, 0, 0)) in (dsa.DSA_ERR_INVALID_ARG, dsa.DSA_ERR_UNSUPPORTED)
+    assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(sh=shape(head_dim=96)) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_ashape_validation_paths():
+    L = dsa.lib()
+    heads = (ctypes.c_int32 * 1)(2)
+    sh = shape()
+    assert L.build_index_ashape(ctypes.byref(sh), heads, 1, -1, 8, vs_c(), None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 4, 0, vs_c(), None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 32, 8, vs_c(16, 16), None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 4, 8, vs_c(null=True), None) == dsa.DSA_ERR_INVALID_ARG
