@@ -79,7 +79,7 @@ __device__ bool range_all(const uint32_t* bm, int lo, int hi) {
 }
 
 // Set the bits of the listed columns (vbits) and diagonals (sbits, stored with
-// one leading pad word so that windows starting at negative offsets read 0).
+// two leading pad words so that windows starting at negative offsets read 0).
 __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
   const int hi = blockIdx.y;
   if (hi >= L.n) return;
@@ -95,7 +95,7 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
       if (j >= 0 && j < a.Nk) atomicOr(&vb[j >> 5], 1u << (j & 31));
     } else {
       int o = diags[i - nc];
-      if (o >= 0 && o < a.Nk) atomicOr(&sb[(o >> 5) + 1], 1u << (o & 31));
+      if (o >= 0 && o < a.Nk) atomicOr(&sb[(o >> 5) + 2], 1u << (o & 31));
     }
   }
 }
@@ -105,7 +105,7 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
 // bit; a >= 1 is "full" (no mask needed) iff all of them are set.
 __global__ __launch_bounds__(256) void vs_tiles_kernel(AttnArgs a, BhList L, int TA) {
   const int bh = L.bh[blockIdx.x];
-  const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 1;     // unpadded view
+  const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
   uint32_t* ab = a.abits + (size_t)bh * a.aw;
   uint32_t* fb = a.fbits + (size_t)bh * a.aw;
   int32_t* al = a.alist + (size_t)bh * a.acap;
@@ -141,139 +141,121 @@ __global__ __launch_bounds__(256) void vs_tiles_kernel(AttnArgs a, BhList L, int
 }
 
 // ---------------------------------------------------------------- main kernel
-struct TileRegs {
-  u32x4 k[8];
-  u32x4 v[8];
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// 16 bytes per lane straight from global memory into LDS; lane l of the wave
+// lands at lds_base + 16 l (lds_base is wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS layouts (both [64 keys][256 bytes], 16-byte chunks XOR-swizzled by row):
+//   K: chunk c of row r at c ^ (r & 15)      -> conflict-free ds_read_b128 of 16 rows
+//   V: chunk c of row r at c ^ 4 (r & 3)     -> conflict-free ds_read_b64_tr_b16
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
 
 struct Entry {
   int mode;    // M_*
-  int kt;      // key tile (tiles) or gather chunk (M_GATHER)
-  int cnt;     // valid keys in a gather chunk
+  int kt;      // key tile, or gather chunk for M_GATHER
+  int cnt;     // valid keys of a gather chunk
 };
-
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                          int Nk, const Entry& e, const int32_t* s_cols, TileRegs& r) {
-  const int tid = threadIdx.x;
-  const int c16 = tid & 15;
-  const int r0 = tid >> 4;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  if (e.mode == M_EMPTY) return;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = r0 + 8 * i;
-    int key;
-    bool ok;
-    if (e.mode == M_GATHER) {
-      ok = rr < e.cnt;
-      key = ok ? s_cols[e.kt * TK + rr] : 0;
-    } else {
-      key = e.kt * TK + rr;
-      ok = key < Nk;
-    }
-    r.k[i] = ok ? *(const u32x4*)(kb + (size_t)key * 128 + c16 * 8) : zero;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kq = r0 + 8 * i;
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int rr = 4 * kq + e4;
-      int key;
-      bool ok;
-      if (e.mode == M_GATHER) {
-        ok = rr < e.cnt;
-        key = ok ? s_cols[e.kt * TK + rr] : 0;
-      } else {
-        key = e.kt * TK + rr;
-        ok = key < Nk;
-      }
-      r.v[4 * i + e4] = ok ? *(const u32x4*)(vb + (size_t)key * 128 + c16 * 8) : zero;
-    }
-  }
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* s_k, uint16_t* s_v) {
-  const int tid = threadIdx.x;
-  const int c16 = tid & 15;
-  const int r0 = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = r0 + 8 * i;
-    *(u32x4*)(s_k + rr * 128 + ((c16 ^ (rr & 15)) * 8)) = r.k[i];
-  }
-  // V^T: row d (128 of them) holds 64 keys; this thread owns d = 8*c16 .. +7 and
-  // key quads kq = r0, r0 + 8.
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kq = r0 + 8 * i;
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = 8 * c16 + dd;
-      const int wsel = dd >> 1;
-      uint32_t x0 = r.v[4 * i + 0][wsel], x1 = r.v[4 * i + 1][wsel];
-      uint32_t x2 = r.v[4 * i + 2][wsel], x3 = r.v[4 * i + 3][wsel];
-      uint32_t lo, hi;
-      if (dd & 1) {
-        lo = (x0 >> 16) | (x1 & 0xffff0000u);
-        hi = (x2 >> 16) | (x3 & 0xffff0000u);
-      } else {
-        lo = (x0 & 0xffffu) | (x1 << 16);
-        hi = (x2 & 0xffffu) | (x3 << 16);
-      }
-      u32x2 pk = {lo, hi};
-      *(u32x2*)(s_v + d * TK + ((kq ^ (d & 15)) * 4)) = pk;
-    }
-  }
-}
 
 struct ItemCtx {
   int b, h, kvh, kind, t, P0, nrows, tq, last_pos;
-  const int32_t* alist;   // VS
+  const int32_t* alist;    // VS strips (tile offsets, ascending)
   int nstrip;
   const uint32_t* fbits;
-  const uint32_t* sbits;  // padded
+  const uint32_t* sbits;   // padded by two leading words
   const uint32_t* vbits;
-  const int32_t* blist;   // BLOCK
+  const int32_t* blist;    // BLOCK
   int nblk, per;
-  int ngather;            // staged this round
+  int ngather;             // staged this round
   int nent;
 };
 
-__device__ __forceinline__ Entry entry_of(const ItemCtx& c, int n) {
+// raw source value of entry n: the tile offset (VS strip) or block id (BLOCK)
+__device__ __forceinline__ int entry_raw(const ItemCtx& c, int n) {
+  if (n >= c.nent) return 0;
+  if (c.kind == 1) return n < c.nstrip ? c.alist[n] : 0;
+  if (c.kind == 2) return c.blist[n / c.per];
+  return 0;
+}
+
+__device__ __forceinline__ Entry entry_of(const ItemCtx& c, int n, int raw) {
   Entry e;
   e.cnt = 0;
-  if (c.kind == 1) {                       // VS
+  if (c.kind == 1) {
     if (n < c.nstrip) {
-      const int a = c.alist[n];
-      e.kt = c.tq - a;
-      e.mode = (a >= 1 && test_bit(c.fbits, a)) ? M_NONE : M_VS;
+      e.kt = c.tq - raw;
+      e.mode = (raw >= 1 && test_bit(c.fbits, raw)) ? M_NONE : M_VS;
     } else {
       const int ch = n - c.nstrip;
       e.kt = ch;
       e.cnt = min(TK, c.ngather - ch * TK);
       e.mode = M_GATHER;
     }
-  } else if (c.kind == 2) {                // BLOCK
-    const int J = c.blist[n / c.per];
-    e.kt = J * c.per + n % c.per;
-    if (J < 0 || e.kt * TK > c.last_pos) e.mode = M_EMPTY;
+  } else if (c.kind == 2) {
+    e.kt = raw * c.per + n % c.per;
+    if (raw < 0 || e.kt * TK > c.last_pos) e.mode = M_EMPTY;
     else e.mode = (e.kt * TK + TK - 1 > c.P0) ? M_CAUSAL : M_NONE;
-  } else {                                 // DENSE
+  } else {
     e.kt = n;
     e.mode = (e.kt * TK + TK - 1 > c.P0) ? M_CAUSAL : M_NONE;
   }
   return e;
 }
 
-__global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched sc) {
-  __shared__ __align__(16) uint16_t s_k[TK * 128];
-  __shared__ __align__(16) uint16_t s_v[128 * TK];
+// Issue the DMA of one 64-key tile of K or V (rows = keys) into LDS.
+template <bool IS_V>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ base, int Nk, const Entry& e,
+                                           const int32_t* s_cols, char* lds, int w, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int blk = 2 * j + w;                 // which 1 KB (4 rows) this wave-instruction fills
+    const int r = blk * 4 + (lane >> 4);
+    const int pc = lane & 15;
+    const int c = IS_V ? swz_v(r, pc) : swz_k(r, pc);
+    int key;
+    if (e.mode == M_GATHER) key = s_cols[e.kt * TK + (r < e.cnt ? r : 0)];
+    else key = min(e.kt * TK + r, Nk - 1);
+    dma16(base + (size_t)key * 128 + c * 8, (lds_void_t*)(lds + blk * 1024));
+  }
+}
+
+struct MaskWords {
+  uint32_t s0, s1, s2;   // diagonal bits window (VS)
+  uint32_t v0, v1;       // column bits of the key tile (VS)
+};
+
+__device__ __forceinline__ void issue_mask_loads(const ItemCtx& c, const Entry& e, int iq, bool row_ok, MaskWords& mw) {
+  if (e.mode != M_VS) return;
+  // offsets o = iq - key for keys kt*64 + 0..63: window [iq - 64 kt - 63, iq - 64 kt]
+  const int lo = iq - e.kt * TK - 63;
+  const int wi = row_ok ? (lo >> 5) + 2 : 0;   // lo >= -63 on real rows, so wi >= 0 (two pad words)
+  mw.s0 = c.sbits[wi];
+  mw.s1 = c.sbits[wi + 1];
+  mw.s2 = c.sbits[wi + 2];
+  mw.v0 = c.vbits[2 * e.kt];
+  mw.v1 = c.vbits[2 * e.kt + 1];
+}
+
+__device__ __forceinline__ uint64_t causal_mask64(int top) {   // bits c <= top
+  return top < 0 ? 0ull : (top >= 63 ? ~0ull : ((2ull << top) - 1ull));
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(const AttnArgs a, const Sched sc) {
+  __shared__ __align__(1024) char s_k[TK * 256];
+  __shared__ __align__(1024) char s_v[TK * 256];
   __shared__ int32_t s_cols[GCAP];
   __shared__ int s_misc[4];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int qn = l & 31;
   const int hh = l >> 5;
@@ -314,9 +296,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched 
       const uint16_t* vbp = a.v + ((size_t)(c.b * a.Hkv + c.kvh) * a.Nk) * 128;
       const uint16_t* qbp = a.q + ((size_t)bh * a.Nq) * 128;
 
-      // Q as the B operand of S^T = K Q^T: lane holds Q[row][16 ks + 8 hh .. +7].
       const int qrow = r0 + 32 * w + qn;
-      const int iq = c.P0 + 32 * w + qn;          // absolute position of the lane's row
+      const int iq = c.P0 + 32 * w + qn;          // absolute position of this lane's row
       const bool row_ok = qrow < a.Nq;
       bf16x8 qf[8];
 #pragma unroll
@@ -325,7 +306,6 @@ __global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched 
         if (row_ok) x = *(const u32x4*)(qbp + (size_t)qrow * 128 + 16 * ks + 8 * hh);
         qf[ks] = __builtin_bit_cast(bf16x8, x);
       }
-
       f32x16 acc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -333,14 +313,12 @@ __global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched 
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
-      int gcursor = 0;
-      int gcount = 0;
+      int gcursor = 0, gcount = 0;
       if (c.kind == 1) {
         c.alist = a.alist + (size_t)bh * a.acap;
         c.fbits = a.fbits + (size_t)bh * a.aw;
         c.sbits = a.sbits + (size_t)bh * a.sw;
         c.vbits = a.vbits + (size_t)bh * a.vw;
-        // strips: alist ascending, keep a <= tq
         const int na = a.acount[bh];
         int lo = 0, hi = na;
         while (lo < hi) {
@@ -358,15 +336,16 @@ __global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched 
 
       for (int round = 0;; ++round) {
         if (c.kind == 1) {
-          // stage the next columns of this item: j <= last_pos outside strip tiles
+          // stage this item's columns: 0 <= j <= last_pos, outside the strip tiles
           const int32_t* cols = a.cols + (size_t)bh * a.cols_cap;
           const uint32_t* ab = a.abits + (size_t)bh * a.aw;
           int staged = 0;
           while (gcursor < gcount && staged <= GCAP - NT) {
             const int idx = gcursor + tid;
             bool keep = false;
+            int j = 0;
             if (idx < gcount) {
-              const int j = cols[idx];
+              j = cols[idx];
               keep = (j >= 0) && (j <= c.last_pos) && !test_bit(ab, c.tq - (j >> 6));
             }
             const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
@@ -374,152 +353,159 @@ __global__ __launch_bounds__(NT) void attn_kernel(const AttnArgs a, const Sched 
             if (l == 0) s_misc[1 + w] = __popcll(bal);
             __syncthreads();
             const int off = staged + (w ? s_misc[1] : 0);
-            if (keep) s_cols[off + ballot_rank(bal)] = cols[idx];
+            if (keep) s_cols[off + ballot_rank(bal)] = j;
             staged += s_misc[1] + s_misc[2];
             gcursor += NT;
-            // columns are ascending: stop once past the item's last row
             const int lastc = cols[min(gcursor, gcount) - 1];
             if (lastc > c.last_pos) gcursor = gcount;
           }
           __syncthreads();
           c.ngather = staged;
-          c.nent = (round == 0 ? c.nstrip : 0) + (staged + TK - 1) / TK;
           if (round > 0) c.nstrip = 0;
+          c.nent = c.nstrip + (staged + TK - 1) / TK;
         } else if (c.kind == 2) {
           c.nent = c.nblk * c.per;
         } else {
           c.nent = c.last_pos / TK + 1;
         }
 
-        TileRegs regs;
-        Entry cur, nxt;
+        Entry cur;
+        MaskWords mw = {0u, 0u, 0u, 0u, 0u};
+        int raw_next = 0;
         if (c.nent > 0) {
-          cur = entry_of(c, 0);
-          load_tile(kbp, vbp, a.Nk, cur, s_cols, regs);
+          cur = entry_of(c, 0, entry_raw(c, 0));
+          raw_next = entry_raw(c, 1);
+          if (cur.mode != M_EMPTY) issue_tile<false>(kbp, a.Nk, cur, s_cols, s_k, w, l);
+          issue_mask_loads(c, cur, iq, row_ok, mw);
         }
         for (int n = 0; n < c.nent; ++n) {
-          __syncthreads();
-          if (cur.mode != M_EMPTY) store_tile(regs, s_k, s_v);
-          __syncthreads();
-          if (n + 1 < c.nent) {
-            nxt = entry_of(c, n + 1);
-            load_tile(kbp, vbp, a.Nk, nxt, s_cols, regs);
-          }
-          if (cur.mode != M_EMPTY) {
-            // ---- masks of the two 32-key halves for this lane's row
-            uint32_t M[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              uint32_t m = ~0u;
-              if (cur.mode == M_GATHER) {
-                m = 0u;
-                const int sbase = cur.kt * TK + 32 * kb + 4 * hh;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                  for (int ii = 0; ii < 4; ++ii) {
-                    const int slot = 32 * kb + 4 * hh + 8 * j + ii;
-                    if (slot < cur.cnt && s_cols[sbase + 8 * j + ii] <= iq) m |= 1u << (8 * j + ii);
-                  }
-              } else if (cur.mode != M_NONE && row_ok) {
-                const int kbase = cur.kt * TK + 32 * kb + 4 * hh;
-                const int otop = iq - kbase;
-                const uint32_t cm = otop < 0 ? 0u : (otop >= 31 ? ~0u : ((2u << otop) - 1u));
-                if (cur.mode == M_CAUSAL) {
-                  m = cm;
-                } else {
-                  uint32_t W = 0u;
-                  if (otop >= 0) {
-                    const int olo = otop - 31;
-                    const int wi = (olo >> 5) + 1;
-                    const uint64_t two = (uint64_t)c.sbits[wi] | ((uint64_t)c.sbits[wi + 1] << 32);
-                    W = (uint32_t)(two >> (olo & 31));
-                  }
-                  const uint32_t vw = c.vbits[(cur.kt * TK + 32 * kb) >> 5] >> (4 * hh);
-                  m = (__builtin_bitreverse32(W) | vw) & cm;
-                }
-              }
-              if (!row_ok) m = 0u;
-              M[kb] = m;
-            }
-            bool act[2];
-            act[0] = __builtin_amdgcn_ballot_w64(M[0] != 0u) != 0;
-            act[1] = __builtin_amdgcn_ballot_w64(M[1] != 0u) != 0;
+          wait_vm();
+          __syncthreads();                       // K_n visible; every wave is done with V_{n-1}
+          const bool live = cur.mode != M_EMPTY;
+          if (live) issue_tile<true>(vbp, a.Nk, cur, s_cols, s_v, w, l);
 
-            // ---- S^T = K Q^T for the active halves
-            f32x16 sacc[2];
+          // ---- this lane's 64-bit mask over the tile's keys (bit c <-> key kt*64 + c)
+          uint64_t M = ~0ull;
+          if (cur.mode == M_CAUSAL) {
+            M = causal_mask64(iq - cur.kt * TK);
+          } else if (cur.mode == M_VS) {
+            const int lo = iq - cur.kt * TK - 63;
+            const int sh = lo & 31;
+            const uint64_t lo64 = ((uint64_t)mw.s1 << 32) | mw.s0;
+            const uint64_t hi64 = (uint64_t)mw.s2;
+            const uint64_t win = sh ? ((lo64 >> sh) | (hi64 << (64 - sh))) : lo64;   // bit b <-> offset lo + b
+            const uint64_t rev = ((uint64_t)__builtin_bitreverse32((uint32_t)win) << 32) |
+                                 __builtin_bitreverse32((uint32_t)(win >> 32));       // bit c <-> key c
+            M = (rev | (((uint64_t)mw.v1 << 32) | mw.v0)) & causal_mask64(iq - cur.kt * TK);
+          } else if (cur.mode == M_GATHER) {
+            // columns are ascending: keys c < n_le are <= iq
+            const int base = cur.kt * TK;
+            int lo2 = 0, hi2 = cur.cnt;
+            while (lo2 < hi2) {
+              const int mid = (lo2 + hi2) >> 1;
+              if (s_cols[base + mid] <= iq) lo2 = mid + 1; else hi2 = mid;
+            }
+            M = lo2 >= 64 ? ~0ull : ((1ull << lo2) - 1ull);
+          }
+          if (!row_ok) M = 0ull;
+          const bool masked = cur.mode != M_NONE;
+          bool act[2];
+          act[0] = live && __builtin_amdgcn_ballot_w64((uint32_t)M != 0u) != 0;
+          act[1] = live && __builtin_amdgcn_ballot_w64((uint32_t)(M >> 32) != 0u) != 0;
+
+          // ---- S^T = K Q^T
+          f32x16 sacc[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-              for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-              if (act[kb]) {
-                const int row = 32 * kb + qn;
+            for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+            if (act[kb]) {
+              const int row = 32 * kb + qn;
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                  const u32x4 x = *(const u32x4*)(s_k + row * 128 + (((2 * ks + hh) ^ (row & 15)) * 8));
-                  sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf[ks],
-                                                                     sacc[kb], 0, 0, 0);
-                }
+              for (int ks = 0; ks < 8; ++ks) {
+                const u32x4 x = *(const u32x4*)(s_k + row * 256 + swz_k(row, 2 * ks + hh) * 16);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf[ks], sacc[kb],
+                                                                   0, 0, 0);
               }
             }
-            // ---- mask + online softmax (base 2)
-            float mx = -INFINITY;
+          }
+          // ---- mask and online softmax (scores kept raw; scale folded into exp2)
+          float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              if (!act[kb]) continue;
+          for (int kb = 0; kb < 2; ++kb) {
+            if (!act[kb]) continue;
+            const uint32_t mk = (uint32_t)(M >> (32 * kb)) >> (4 * hh);
 #pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int s = 8 * (v >> 2) + (v & 3);
-                float x = sacc[kb][v] * scale2;
-                if (!((M[kb] >> s) & 1u)) x = -INFINITY;
-                sacc[kb][v] = x;
-                mx = fmaxf(mx, x);
-              }
+            for (int v = 0; v < 16; ++v) {
+              float x = sacc[kb][v];
+              if (masked && !((mk >> (8 * (v >> 2) + (v & 3))) & 1u)) x = -INFINITY;
+              sacc[kb][v] = x;
+              mx = fmaxf(mx, x);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const bool grow = mx > m_run + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-              const float mnew = grow ? mx : m_run;
-              const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
-              l_run *= f;
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+          const bool grow = mx > m_run + 8.0f;
+          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float mnew = grow ? mx : m_run;
+            const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
+            l_run *= f;
 #pragma unroll
-              for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[db][v] *= f;
-              m_run = mnew;
+              for (int v = 0; v < 16; ++v) acc[db][v] *= f;
+            m_run = mnew;
+          }
+          const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+          uint32_t pk[2][8];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (!act[kb]) continue;
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale2, -muse));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v + 1], scale2, -muse));
+              // normalise with the same bf16-rounded weights the PV product uses
+              const uint32_t pb = pack_bf16x2(p0, p1);
+              l_run += bf16_lo(pb) + bf16_hi(pb);
+              pk[kb][v >> 1] = pb;
             }
-            const float muse = (m_run == -INFINITY) ? 0.f : m_run;
-            uint32_t pk[2][8];
+          }
+
+          wait_vm();
+          __syncthreads();                       // V_n visible; every wave is done with K_n
+          Entry nxt;
+          nxt.mode = M_EMPTY;
+          if (n + 1 < c.nent) {
+            nxt = entry_of(c, n + 1, raw_next);
+            raw_next = entry_raw(c, n + 2);
+            if (nxt.mode != M_EMPTY) issue_tile<false>(kbp, a.Nk, nxt, s_cols, s_k, w, l);
+            issue_mask_loads(c, nxt, iq, row_ok, mw);
+          }
+
+          // ---- O^T += V^T P^T, keys 16 ks2 .. +15 per step
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              if (!act[kb]) continue;
+          for (int ks2 = 0; ks2 < 4; ++ks2) {
+            const int kb = ks2 >> 1;
+            if (!act[kb]) continue;
+            const int o8 = (ks2 & 1) * 4;
+            u32x4 bx = {pk[kb][o8], pk[kb][o8 + 1], pk[kb][o8 + 2], pk[kb][o8 + 3]};
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
+            const int G = l >> 4, s = l & 15;
+            const int rowa = 16 * ks2 + 4 * (G >> 1) + (s >> 2);
+            const int rowb = rowa + 8;
 #pragma unroll
-              for (int v = 0; v < 16; v += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(sacc[kb][v] - muse);
-                const float p1 = __builtin_amdgcn_exp2f(sacc[kb][v + 1] - muse);
-                // normalise with the same bf16-rounded weights the PV product uses
-                const uint32_t pb = pack_bf16x2(p0, p1);
-                l_run += bf16_lo(pb) + bf16_hi(pb);
-                pk[kb][v >> 1] = pb;
-              }
-            }
-            // ---- O^T += V^T P^T; key step ks2 covers keys 16 ks2 .. +15
-#pragma unroll
-            for (int ks2 = 0; ks2 < 4; ++ks2) {
-              const int kb = ks2 >> 1;
-              if (!act[kb]) continue;
-              const int o8 = (ks2 & 1) * 4;
-              u32x4 bx = {pk[kb][o8], pk[kb][o8 + 1], pk[kb][o8 + 2], pk[kb][o8 + 3]};
-              const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
-              const int ch0 = 4 * ks2 + hh, ch1 = 4 * ks2 + 2 + hh;
-#pragma unroll
-              for (int db = 0; db < 4; ++db) {
-                const int d = 32 * db + qn;
-                const u32x2 y0 = *(const u32x2*)(s_v + d * TK + ((ch0 ^ (d & 15)) * 4));
-                const u32x2 y1 = *(const u32x2*)(s_v + d * TK + ((ch1 ^ (d & 15)) * 4));
-                u32x4 ax = {y0[0], y0[1], y1[0], y1[1]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ax), bop, acc[db], 0, 0, 0);
-              }
+            for (int db = 0; db < 4; ++db) {
+              const int cch = 4 * db + 2 * (G & 1) + ((s & 3) >> 1);
+              const int half = (s & 1) * 8;
+              lds_short4_t* pa = (lds_short4_t*)((__attribute__((address_space(3))) char*)s_v + rowa * 256 +
+                                                 swz_v(rowa, cch) * 16 + half);
+              lds_short4_t* pb2 = (lds_short4_t*)((__attribute__((address_space(3))) char*)s_v + rowb * 256 +
+                                                  swz_v(rowb, cch) * 16 + half);
+              const short4_t ya = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa);
+              const short4_t yb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb2);
+              typedef short short8_t __attribute__((ext_vector_type(8)));
+              const short8_t ab = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
             }
           }
           cur = nxt;
@@ -576,7 +562,7 @@ struct VsLayout {
 
 VsLayout vs_layout(int B, int H, int Nk) {
   VsLayout L;
-  L.sw = (Nk + 31) / 32 + 3;
+  L.sw = (Nk + 31) / 32 + 5;
   L.vw = (Nk + 31) / 32 + 2;
   L.TA = (Nk + TK - 1) / TK + 1;
   L.aw = (L.TA + 31) / 32 + 1;
