@@ -4,29 +4,33 @@
 //   O[i] = sum_{j in M_h(i)} softmax_j(q_i . k_j / sqrt(d)) v_j,  LSE[i] = log sum exp,
 // with M_h(i) given by the head's pattern and index set ("MInference 1.0"
 // explainer, GPU kernels section; authors' abstract: sparse kernels over
-// pattern + indices).  Following "FlashPrefill" section 2.3, the kernel walks
-// compact lists of key tiles (index-driven jumps) rather than testing every tile.
+// pattern + indices).  As "FlashPrefill" section 2.3 prescribes, the kernel
+// walks compact lists of key tiles (index-driven jumps), never testing the
+// tiles it does not need.
 //
-// Design (MI355X):
-//  * one work item = (batch, head, 64-query tile); workgroup = 2 waves, each wave
-//    owns 32 query rows and computes S^T = K Q^T and O^T += V^T P^T with
-//    v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Using S^T makes the MFMA output
-//    of P^T usable directly as the B operand of the PV product (no shuffle).
-//  * K tiles (64 keys) are staged in LDS with a 16-byte XOR swizzle; V tiles are
-//    stored transposed (V^T, 8-byte XOR swizzle) so the PV A operand is two
-//    8-byte LDS reads.  Global loads of tile n+1 are issued before tile n is
-//    computed (register prefetch, single LDS buffer).
-//  * online softmax in fp32 (base 2), P rounded to bf16 for the PV MFMA, lazy
-//    rescaling of the accumulator only when the running max grows by > 8 (log2).
-//  * Vertical-Slash heads: a compile step turns the column/diagonal lists into
-//    bitmaps and the set A of key-tile offsets a touched by a selected diagonal.
-//    Query tile t visits key tiles t - a (slash strips) with an exact per-element
-//    mask (diagonal bit | column bit) and skips each 32x32 sub-block whose mask is
-//    empty; columns outside those tiles are gathered 64 at a time.  Every (i, j)
-//    is visited exactly once, so the set semantics (no double counting) hold.
-//  * persistent workgroups pull items from per-XCD queues (t descending, so the
-//    long causal rows start first) and steal from other queues when theirs is
-//    empty; heads are packed into queues by estimated cost.
+// Design (MI355X, gfx950):
+//  * A work item is (batch, head, pair of adjacent 64-row query tiles): 128 rows,
+//    one workgroup of 4 waves, each wave owning 32 rows.  The pair streams the
+//    union of its two tiles' key-tile lists once, so every K/V tile brought into
+//    LDS serves up to 128 rows; each wave applies its own exact mask and skips
+//    32x32 sub-blocks with no selected entry.
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
+//    the MFMA output of S^T is, after the softmax, exactly the B operand layout
+//    of the PV product, so P never leaves registers.
+//  * K and V tiles travel global -> LDS by DMA (global_load_lds_dwordx4) into a
+//    two-stage ring: tile n+1 is in flight while tile n is computed, one barrier
+//    per tile.  16-byte chunks are XOR-swizzled per row so the ds_read_b128 of K
+//    and the transposing ds_read_b64_tr_b16 of V are bank-conflict free.
+//  * Online softmax in fp32 (base 2, scale folded into the exponent), P rounded
+//    to bf16 for the MFMA and summed in that same rounding (v_dot2_f32_bf16), the
+//    accumulator rescaled lazily (only when the row max grows by > 8 in log2).
+//  * Vertical-Slash heads: a compile step turns the column / diagonal lists into
+//    bitmaps and the set A of key-tile offsets a crossed by a selected diagonal
+//    (pairs use A u (A+1)).  Strip tiles carry an exact per-element mask
+//    (diagonal bit | column bit, causal); columns outside all strip tiles are
+//    gathered 64 at a time.  Every selected (i, j) is visited exactly once.
+//  * Persistent workgroups pull items from per-XCD queues (longest rows first)
+//    and steal from other queues when their own is empty.
 #include "common.h"
 #include "internal.h"
 
@@ -36,16 +40,16 @@
 namespace dsa {
 namespace {
 
-constexpr int TQ = 64;       // query rows per work item
-constexpr int TK = 64;       // keys per tile
-constexpr int NT = 128;      // threads per workgroup
-constexpr int GCAP = 1024;   // gathered columns staged per round
+constexpr int TQ = 64;       // rows per query tile
+constexpr int TK = 64;       // keys per key tile
+constexpr int NT = 256;      // 4 waves: two query tiles x two 32-row halves
+constexpr int GCAP = 2048;   // gathered columns staged per round
 
-enum { M_NONE = 0, M_CAUSAL = 1, M_VS = 2, M_GATHER = 3, M_EMPTY = 4 };
+enum { M_NONE = 0, M_CAUSAL = 1, M_VS = 2, M_GATHER = 3, M_SKIP = 4 };
 
 struct Sched {
   int nq;                       // number of queues
-  int T;                        // query tiles per head
+  int T2;                       // query-tile pairs per head
   int qstart[kMaxQueues + 1];   // heads of queue g: heads[qstart[g] .. qstart[g+1])
   int16_t heads[kMaxHeadTable]; // b * H + h
 };
@@ -100,51 +104,61 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
   }
 }
 
-// Tile offsets a in [0, TA): a is in A iff a selected diagonal crosses some pair
-// (query tile t, key tile t - a), i.e. offsets [64a - 63, 64a + 63] hold a set
-// bit; a >= 1 is "full" (no mask needed) iff all of them are set.
+// Key-tile offsets a in [0, TA).  a is in A iff a selected diagonal crosses
+// some pair (query tile t, key tile t - a), i.e. offsets [64a - 63, 64a + 63]
+// hold a set bit; a >= 1 is "full" (no mask needed) iff all of them are set.
+// A query-tile pair (t, t + 1) visits key tiles t + 1 - a for a in A2 = A u (A+1);
+// A2 is written as an ascending list and as a bitmap.
 __global__ __launch_bounds__(256) void vs_tiles_kernel(AttnArgs a, BhList L, int TA) {
   const int bh = L.bh[blockIdx.x];
   const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
-  uint32_t* ab = a.abits + (size_t)bh * a.aw;
   uint32_t* fb = a.fbits + (size_t)bh * a.aw;
-  int32_t* al = a.alist + (size_t)bh * a.acap;
+  uint32_t* a2b = a.a2bits + (size_t)bh * a.aw;
+  int32_t* al = a.a2list + (size_t)bh * a.acap;
+  int32_t* ale = a.a2le + (size_t)bh * a.acap;
   __shared__ int s_wave[4];
   __shared__ int s_base;
   if (threadIdx.x == 0) s_base = 0;
   __syncthreads();
   const int w = threadIdx.x >> 6;
+  auto in_a = [&](int t) {
+    if (t < 0 || t >= TA) return false;
+    const int lo = max(0, 64 * t - 63), hi = min(a.Nk - 1, 64 * t + 63);
+    return lo <= hi && range_any(sb, lo, hi);
+  };
   for (int a0 = 0; a0 < TA; a0 += 256) {
     const int t = a0 + threadIdx.x;
-    bool inA = false, full = false;
+    bool in2 = false;
     if (t < TA) {
-      const int lo = max(0, 64 * t - 63), hi = min(a.Nk - 1, 64 * t + 63);
-      if (lo <= hi) {
-        inA = range_any(sb, lo, hi);
-        full = (t >= 1) && inA && range_all(sb, lo, hi);
+      const bool inA = in_a(t);
+      in2 = inA || in_a(t - 1);
+      if (inA && t >= 1) {
+        const int lo = 64 * t - 63, hi = min(a.Nk - 1, 64 * t + 63);
+        if (lo <= hi && range_all(sb, lo, hi)) atomicOr(&fb[t >> 5], 1u << (t & 31));
       }
-      if (inA) atomicOr(&ab[t >> 5], 1u << (t & 31));
-      if (full) atomicOr(&fb[t >> 5], 1u << (t & 31));
+      if (in2) atomicOr(&a2b[t >> 5], 1u << (t & 31));
     }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(inA);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(in2);
     const uint32_t rank = ballot_rank(bal);
     if ((threadIdx.x & 63) == 0) s_wave[w] = __popcll(bal);
     __syncthreads();
     int off = s_base;
     for (int i = 0; i < w; ++i) off += s_wave[i];
-    if (inA) al[off + rank] = t;
+    if (in2) al[off + rank] = t;
+    if (t < TA) ale[t] = off + rank + (in2 ? 1 : 0);     // #{a in A2 : a <= t}
     __syncthreads();
     if (threadIdx.x == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.acount[bh] = s_base;
+  if (threadIdx.x == 0) a.a2count[bh] = s_base;
 }
 
 // ---------------------------------------------------------------- main kernel
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // 16 bytes per lane straight from global memory into LDS; lane l of the wave
 // lands at lds_base + 16 l (lds_base is wave-uniform).
@@ -153,151 +167,188 @@ __device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// LDS layouts (both [64 keys][256 bytes], 16-byte chunks XOR-swizzled by row):
+// LDS tiles are [64 keys][256 bytes] with 16-byte chunks XOR-swizzled by row:
 //   K: chunk c of row r at c ^ (r & 15)      -> conflict-free ds_read_b128 of 16 rows
 //   V: chunk c of row r at c ^ 4 (r & 3)     -> conflict-free ds_read_b64_tr_b16
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
 
+// One entry of a pair's tile stream.
 struct Entry {
-  int mode;    // M_*
-  int kt;      // key tile, or gather chunk for M_GATHER
+  int kind;    // 0 key tile, 1 gather chunk, -1 none
+  int kt;      // key tile index, or gather chunk index
   int cnt;     // valid keys of a gather chunk
+  int flags;   // bit h: query tile h of the pair uses this entry
 };
 
-struct ItemCtx {
-  int b, h, kvh, kind, t, P0, nrows, tq, last_pos;
-  const int32_t* alist;    // VS strips (tile offsets, ascending)
+struct Item {
+  int bh, kvh, kind, P0, last_pos, tq1;
+  // VS
+  const int32_t* a2;       // strip tile offsets (relative to tq1), ascending
   int nstrip;
-  const uint32_t* fbits;
-  const uint32_t* sbits;   // padded by two leading words
-  const uint32_t* vbits;
-  const int32_t* blist;    // BLOCK
-  int nblk, per;
-  int ngather;             // staged this round
-  int nent;
+  // BLOCK
+  const int32_t* l0;       // list of query block I0 (or of the shared block)
+  const int32_t* l1;       // list of query block I0 + 1 (block 64 only)
+  int n0, n1, per;
+  // stream
+  int nent, ngather;
 };
 
-// raw source value of entry n: the tile offset (VS strip) or block id (BLOCK)
-__device__ __forceinline__ int entry_raw(const ItemCtx& c, int n) {
-  if (n >= c.nent) return 0;
-  if (c.kind == 1) return n < c.nstrip ? c.alist[n] : 0;
-  if (c.kind == 2) return c.blist[n / c.per];
-  return 0;
+// Cursor over a pair's entries.  The global-memory lookups of entry n + 1 are
+// issued while entry n is being processed (one step of prefetch).
+struct Cursor {
+  int n;                   // index of the next entry
+  int raw;                 // prefetched value for entry n (VS strip / shared block list)
+  int i0, i1, x0, x1;      // two-list merge state (block 64): heads of both lists
+  int x0n, x1n;            // prefetched successors of the heads
+};
+
+__device__ __forceinline__ int list_at(const int32_t* L, int n, int i) { return i < n ? L[i] : 0x7fffffff; }
+
+__device__ __forceinline__ void cursor_init(const Item& it, Cursor& c) {
+  c.n = 0;
+  c.raw = 0;
+  c.i0 = c.i1 = 0;
+  c.x0 = c.x1 = c.x0n = c.x1n = 0x7fffffff;
+  if (it.kind == 1) c.raw = it.nstrip > 0 ? it.a2[0] : 0;
+  else if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? it.l0[0] : 0;
+  else if (it.kind == 2) {
+    c.x0 = list_at(it.l0, it.n0, 0); c.x1 = list_at(it.l1, it.n1, 0);
+    c.x0n = list_at(it.l0, it.n0, 1); c.x1n = list_at(it.l1, it.n1, 1);
+  }
 }
 
-__device__ __forceinline__ Entry entry_of(const ItemCtx& c, int n, int raw) {
+__device__ __forceinline__ bool cursor_has_next(const Item& it, const Cursor& c) {
+  if (it.kind == 2 && it.per == 1) return min(c.x0, c.x1) != 0x7fffffff;
+  return c.n < it.nent;
+}
+
+// Produce entry c.n and advance.  Valid only while cursor_has_next().
+__device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   Entry e;
   e.cnt = 0;
-  if (c.kind == 1) {
-    if (n < c.nstrip) {
-      e.kt = c.tq - raw;
-      e.mode = (raw >= 1 && test_bit(c.fbits, raw)) ? M_NONE : M_VS;
+  e.flags = 3;
+  e.kind = 0;
+  const int n = c.n++;
+  if (it.kind == 1) {
+    if (n < it.nstrip) {
+      e.kt = it.tq1 - c.raw;
+      c.raw = (n + 1 < it.nstrip) ? it.a2[n + 1] : 0;
     } else {
-      const int ch = n - c.nstrip;
-      e.kt = ch;
-      e.cnt = min(TK, c.ngather - ch * TK);
-      e.mode = M_GATHER;
+      e.kind = 1;
+      e.kt = n - it.nstrip;
+      e.cnt = min(TK, it.ngather - e.kt * TK);
     }
-  } else if (c.kind == 2) {
-    e.kt = raw * c.per + n % c.per;
-    if (raw < 0 || e.kt * TK > c.last_pos) e.mode = M_EMPTY;
-    else e.mode = (e.kt * TK + TK - 1 > c.P0) ? M_CAUSAL : M_NONE;
+  } else if (it.kind == 2 && it.per == 2) {
+    e.kt = c.raw * 2 + (n & 1);
+    if (n & 1) c.raw = ((n >> 1) + 1 < it.n0) ? it.l0[(n >> 1) + 1] : 0;
+  } else if (it.kind == 2) {
+    const int x = min(c.x0, c.x1);
+    e.kt = x;
+    e.flags = (c.x0 == x ? 1 : 0) | (c.x1 == x ? 2 : 0);
+    if (c.x0 == x) { ++c.i0; c.x0 = c.x0n; c.x0n = list_at(it.l0, it.n0, c.i0 + 1); }
+    if (c.x1 == x) { ++c.i1; c.x1 = c.x1n; c.x1n = list_at(it.l1, it.n1, c.i1 + 1); }
   } else {
     e.kt = n;
-    e.mode = (e.kt * TK + TK - 1 > c.P0) ? M_CAUSAL : M_NONE;
   }
+  // out-of-range block ids or tiles beyond the pair's last row contribute nothing
+  if (e.kind == 0 && (e.kt < 0 || e.kt * TK > it.last_pos)) e.flags = 0;
   return e;
 }
 
-// Issue the DMA of one 64-key tile of K or V (rows = keys) into LDS.
+// DMA of one 64-key tile of K or V into LDS.  Wave w fills the 1 KB blocks
+// 4j + w, i.e. rows 16j + rl with rl = 4w + lane/16.  A full tile is a
+// wave-uniform base plus this lane's constant offset; a partial tile or a
+// gather chunk computes each row's key.
 template <bool IS_V>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ base, int Nk, const Entry& e,
-                                           const int32_t* s_cols, char* lds, int w, int lane) {
+                                           const int32_t* s_cols, char* lds, int w, int lane, uint32_t off) {
+  if (e.flags == 0) return;
+  if (e.kind == 0 && e.kt * TK + TK <= Nk) {
+    const char* tb = (const char*)(base + (size_t)e.kt * TK * 128);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int blk = 2 * j + w;                 // which 1 KB (4 rows) this wave-instruction fills
-    const int r = blk * 4 + (lane >> 4);
-    const int pc = lane & 15;
-    const int c = IS_V ? swz_v(r, pc) : swz_k(r, pc);
+    for (int j = 0; j < 4; ++j) dma16(tb + off + 4096 * j, (lds_void_t*)(lds + (4 * j + w) * 1024));
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * j + 4 * w + (lane >> 4);
+    const int c = IS_V ? swz_v(r, lane & 15) : swz_k(r, lane & 15);
     int key;
-    if (e.mode == M_GATHER) key = s_cols[e.kt * TK + (r < e.cnt ? r : 0)];
+    if (e.kind == 1) key = s_cols[e.kt * TK + (r < e.cnt ? r : 0)];
     else key = min(e.kt * TK + r, Nk - 1);
-    dma16(base + (size_t)key * 128 + c * 8, (lds_void_t*)(lds + blk * 1024));
+    dma16(base + (size_t)key * 128 + c * 8, (lds_void_t*)(lds + (4 * j + w) * 1024));
   }
 }
 
-struct MaskWords {
-  uint32_t s0, s1, s2;   // diagonal bits window (VS)
-  uint32_t v0, v1;       // column bits of the key tile (VS)
-};
-
-__device__ __forceinline__ void issue_mask_loads(const ItemCtx& c, const Entry& e, int iq, bool row_ok, MaskWords& mw) {
-  if (e.mode != M_VS) return;
-  // offsets o = iq - key for keys kt*64 + 0..63: window [iq - 64 kt - 63, iq - 64 kt]
-  const int lo = iq - e.kt * TK - 63;
-  const int wi = row_ok ? (lo >> 5) + 2 : 0;   // lo >= -63 on real rows, so wi >= 0 (two pad words)
-  mw.s0 = c.sbits[wi];
-  mw.s1 = c.sbits[wi + 1];
-  mw.s2 = c.sbits[wi + 2];
-  mw.v0 = c.vbits[2 * e.kt];
-  mw.v1 = c.vbits[2 * e.kt + 1];
+__device__ __forceinline__ uint32_t causal_mask32(int top) {   // bits c <= top
+  return top < 0 ? 0u : (top >= 31 ? ~0u : ((2u << top) - 1u));
 }
 
-__device__ __forceinline__ uint64_t causal_mask64(int top) {   // bits c <= top
-  return top < 0 ? 0ull : (top >= 63 ? ~0ull : ((2ull << top) - 1ull));
-}
+#ifndef DSA_ATTN_WAVES_PER_SIMD
+#define DSA_ATTN_WAVES_PER_SIMD 2
+#endif
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(const AttnArgs a, const Sched sc) {
-  __shared__ __align__(1024) char s_k[TK * 256];
-  __shared__ __align__(1024) char s_v[TK * 256];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_SIMD))) void attn_kernel(
+    const AttnArgs a, const Sched sc) {
+  __shared__ __align__(1024) char s_kv[2][2][TK * 256];   // [stage][0 = K, 1 = V]
   __shared__ int32_t s_cols[GCAP];
-  __shared__ int s_misc[4];
+  __shared__ int s_misc[8];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ih = w >> 1;               // which query tile of the pair
+  const int wr = w & 1;                // which 32-row half of that tile
   const int l = tid & 63;
   const int qn = l & 31;
   const int hh = l >> 5;
   const float scale2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int rep = a.H / a.Hkv;
   const int myq = blockIdx.x % sc.nq;
+  const int rl = 4 * w + (l >> 4);
+  const uint32_t off_k = rl * 256 + (((l & 15) ^ (rl & 15)) * 16);
+  const uint32_t off_v = rl * 256 + (((l & 15) ^ ((rl & 3) << 2)) * 16);
+  // lane-constant parts of the V fragment addresses
+  const int G = l >> 4, si = l & 15;
+  const int v_row0 = 4 * (G >> 1) + (si >> 2);           // + 32 kb + 16 s2 (+ 8)
+  const int v_half = (si & 1) * 8;
 
   for (int qi = 0; qi < sc.nq; ++qi) {
     const int g = (myq + qi) % sc.nq;
     const int nh = sc.qstart[g + 1] - sc.qstart[g];
-    const int nitems = nh * sc.T;
+    const int nitems = nh * sc.T2;
     if (nh == 0) continue;
     while (true) {
       __syncthreads();
       if (tid == 0) s_misc[0] = atomicAdd(&a.counters[g], 1);
       __syncthreads();
-      const int it = s_misc[0];
-      if (it >= nitems) break;
+      const int itn = s_misc[0];
+      if (itn >= nitems) break;
 
-      ItemCtx c;
-      const int bh = sc.heads[sc.qstart[g] + it % nh];
-      c.b = bh / a.H;
-      c.h = bh % a.H;
-      c.kvh = c.h / rep;
-      c.kind = a.kind[c.h];
-      c.t = sc.T - 1 - it / nh;
-      const int r0 = c.t * TQ;
-      c.nrows = min(TQ, a.Nq - r0);
-      c.P0 = r0 + a.q_offset;
-      c.last_pos = c.P0 + c.nrows - 1;
-      c.tq = c.P0 / TK;
-      c.nstrip = 0;
-      c.ngather = 0;
-      c.per = 1;
-      c.nblk = 0;
+      Item it;
+      it.bh = sc.heads[sc.qstart[g] + itn % nh];
+      const int b = it.bh / a.H, h = it.bh % a.H;
+      it.kvh = h / rep;
+      it.kind = a.kind[h];
+      const int p = sc.T2 - 1 - itn / nh;
+      const int r0 = p * 2 * TQ;
+      it.P0 = r0 + a.q_offset;
+      it.last_pos = min(a.Nq, r0 + 2 * TQ) - 1 + a.q_offset;
+      it.tq1 = it.P0 / TK + 1;
+      it.nstrip = 0;
+      it.ngather = 0;
+      it.per = 1;
+      it.n0 = it.n1 = 0;
+      it.a2 = nullptr;
+      it.l0 = it.l1 = nullptr;
 
-      const uint16_t* kbp = a.k + ((size_t)(c.b * a.Hkv + c.kvh) * a.Nk) * 128;
-      const uint16_t* vbp = a.v + ((size_t)(c.b * a.Hkv + c.kvh) * a.Nk) * 128;
-      const uint16_t* qbp = a.q + ((size_t)bh * a.Nq) * 128;
+      const uint16_t* kbp = a.k + ((size_t)(b * a.Hkv + it.kvh) * a.Nk) * 128;
+      const uint16_t* vbp = a.v + ((size_t)(b * a.Hkv + it.kvh) * a.Nk) * 128;
+      const uint16_t* qbp = a.q + ((size_t)it.bh * a.Nq) * 128;
 
-      const int qrow = r0 + 32 * w + qn;
-      const int iq = c.P0 + 32 * w + qn;          // absolute position of this lane's row
+      const int qrow = r0 + TQ * ih + 32 * wr + qn;
+      const int P0w = it.P0 + TQ * ih;                // first position of this wave's query tile
+      const int iq = P0w + 32 * wr + qn;               // absolute position of this lane's row
       const bool row_ok = qrow < a.Nq;
       bf16x8 qf[8];
 #pragma unroll
@@ -313,32 +364,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
+      const uint32_t* fbits = nullptr;
+      const uint32_t* sbits = nullptr;
+      const uint32_t* vbits = nullptr;
       int gcursor = 0, gcount = 0;
-      if (c.kind == 1) {
-        c.alist = a.alist + (size_t)bh * a.acap;
-        c.fbits = a.fbits + (size_t)bh * a.aw;
-        c.sbits = a.sbits + (size_t)bh * a.sw;
-        c.vbits = a.vbits + (size_t)bh * a.vw;
-        const int na = a.acount[bh];
-        int lo = 0, hi = na;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (c.alist[mid] <= c.tq) lo = mid + 1; else hi = mid;
+      if (it.kind == 1) {
+        it.a2 = a.a2list + (size_t)it.bh * a.acap;
+        fbits = a.fbits + (size_t)it.bh * a.aw;
+        sbits = a.sbits + (size_t)it.bh * a.sw;
+        vbits = a.vbits + (size_t)it.bh * a.vw;
+        it.nstrip = a.a2le[(size_t)it.bh * a.acap + it.tq1];
+        gcount = min(a.cols_count[it.bh], a.cols_cap);
+      } else if (it.kind == 2) {
+        it.per = a.block / TK;
+        const int I0 = it.P0 / a.block;
+        it.l0 = a.bidx + ((size_t)it.bh * a.nqb + I0) * a.bcap;
+        it.n0 = min(a.bcount[(size_t)it.bh * a.nqb + I0], a.bcap);
+        it.l1 = it.l0;
+        if (it.per == 1 && I0 + 1 < a.nqb && r0 + TQ < a.Nq) {
+          it.l1 = a.bidx + ((size_t)it.bh * a.nqb + I0 + 1) * a.bcap;
+          it.n1 = min(a.bcount[(size_t)it.bh * a.nqb + I0 + 1], a.bcap);
         }
-        c.nstrip = lo;
-        gcount = min(a.cols_count[bh], a.cols_cap);
-      } else if (c.kind == 2) {
-        const int I = c.P0 / a.block;
-        c.blist = a.bidx + ((size_t)bh * a.nqb + I) * a.bcap;
-        c.nblk = min(a.bcount[(size_t)bh * a.nqb + I], a.bcap);
-        c.per = a.block / TK;
       }
 
       for (int round = 0;; ++round) {
-        if (c.kind == 1) {
-          // stage this item's columns: 0 <= j <= last_pos, outside the strip tiles
-          const int32_t* cols = a.cols + (size_t)bh * a.cols_cap;
-          const uint32_t* ab = a.abits + (size_t)bh * a.aw;
+        if (it.kind == 1) {
+          // stage this pair's columns: 0 <= j <= last_pos and outside every strip tile
+          const int32_t* cols = a.cols + (size_t)it.bh * a.cols_cap;
+          const uint32_t* a2b = a.a2bits + (size_t)it.bh * a.aw;
           int staged = 0;
           while (gcursor < gcount && staged <= GCAP - NT) {
             const int idx = gcursor + tid;
@@ -346,178 +399,209 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
             int j = 0;
             if (idx < gcount) {
               j = cols[idx];
-              keep = (j >= 0) && (j <= c.last_pos) && !test_bit(ab, c.tq - (j >> 6));
+              keep = (j >= 0) && (j <= it.last_pos) && !test_bit(a2b, it.tq1 - (j >> 6));
             }
             const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
             __syncthreads();
             if (l == 0) s_misc[1 + w] = __popcll(bal);
             __syncthreads();
-            const int off = staged + (w ? s_misc[1] : 0);
+            int off = staged;
+            for (int i = 0; i < w; ++i) off += s_misc[1 + i];
             if (keep) s_cols[off + ballot_rank(bal)] = j;
-            staged += s_misc[1] + s_misc[2];
+            staged += s_misc[1] + s_misc[2] + s_misc[3] + s_misc[4];
             gcursor += NT;
             const int lastc = cols[min(gcursor, gcount) - 1];
-            if (lastc > c.last_pos) gcursor = gcount;
+            if (lastc > it.last_pos) gcursor = gcount;
           }
           __syncthreads();
-          c.ngather = staged;
-          if (round > 0) c.nstrip = 0;
-          c.nent = c.nstrip + (staged + TK - 1) / TK;
-        } else if (c.kind == 2) {
-          c.nent = c.nblk * c.per;
+          it.ngather = staged;
+          if (round > 0) it.nstrip = 0;
+          it.nent = it.nstrip + (staged + TK - 1) / TK;
+        } else if (it.kind == 2) {
+          // per == 2: one shared list; per == 1: the cursor merges two lists and
+          // stops when both are exhausted (nent is only an upper bound)
+          it.nent = it.per == 2 ? 2 * it.n0 : it.n0 + it.n1;
         } else {
-          c.nent = c.last_pos / TK + 1;
+          it.nent = it.last_pos / TK + 1;
         }
 
+        Cursor cc;
+        cursor_init(it, cc);
         Entry cur;
-        MaskWords mw = {0u, 0u, 0u, 0u, 0u};
-        int raw_next = 0;
-        if (c.nent > 0) {
-          cur = entry_of(c, 0, entry_raw(c, 0));
-          raw_next = entry_raw(c, 1);
-          if (cur.mode != M_EMPTY) issue_tile<false>(kbp, a.Nk, cur, s_cols, s_k, w, l);
-          issue_mask_loads(c, cur, iq, row_ok, mw);
+        cur.kind = -1;
+        cur.flags = 0;
+        uint32_t ms0 = 0u, ms1 = 0u, ms2 = 0u, mv0 = 0u, mv1 = 0u;
+        bool have = cursor_has_next(it, cc);
+        if (have) {
+          cur = cursor_next(it, cc);
+          issue_tile<false>(kbp, a.Nk, cur, s_cols, s_kv[0][0], w, l, off_k);
+          issue_tile<true>(vbp, a.Nk, cur, s_cols, s_kv[0][1], w, l, off_v);
+          if (it.kind == 1 && cur.kind == 0) {
+            // offsets iq - key for the 64 keys of the tile: window [top - 63, top]
+            const int wi = row_ok ? max(((iq - cur.kt * TK - 63) >> 5) + 2, 0) : 0;
+            ms0 = sbits[wi]; ms1 = sbits[wi + 1]; ms2 = sbits[wi + 2];
+            mv0 = vbits[2 * cur.kt]; mv1 = vbits[2 * cur.kt + 1];
+          }
         }
-        for (int n = 0; n < c.nent; ++n) {
+        for (int n = 0; have; ++n) {
+          const int stage = n & 1;
           wait_vm();
-          __syncthreads();                       // K_n visible; every wave is done with V_{n-1}
-          const bool live = cur.mode != M_EMPTY;
-          if (live) issue_tile<true>(vbp, a.Nk, cur, s_cols, s_v, w, l);
+          __syncthreads();                       // tile n landed; every wave is done with tile n - 1
+          Entry nxt;
+          nxt.kind = -1;
+          nxt.flags = 0;
+          uint32_t ns0 = 0u, ns1 = 0u, ns2 = 0u, nv0 = 0u, nv1 = 0u;
+          const bool have_n = cursor_has_next(it, cc);
+          if (have_n) {
+            nxt = cursor_next(it, cc);
+            issue_tile<false>(kbp, a.Nk, nxt, s_cols, s_kv[stage ^ 1][0], w, l, off_k);
+            issue_tile<true>(vbp, a.Nk, nxt, s_cols, s_kv[stage ^ 1][1], w, l, off_v);
+            if (it.kind == 1 && nxt.kind == 0) {
+              const int wi = row_ok ? max(((iq - nxt.kt * TK - 63) >> 5) + 2, 0) : 0;
+              ns0 = sbits[wi]; ns1 = sbits[wi + 1]; ns2 = sbits[wi + 2];
+              nv0 = vbits[2 * nxt.kt]; nv1 = vbits[2 * nxt.kt + 1];
+            }
+          }
+          const char* sk = s_kv[stage][0];
+          const lds_char_t* sv = (const lds_char_t*)s_kv[stage][1];
 
-          // ---- this lane's 64-bit mask over the tile's keys (bit c <-> key kt*64 + c)
-          uint64_t M = ~0ull;
-          if (cur.mode == M_CAUSAL) {
-            M = causal_mask64(iq - cur.kt * TK);
-          } else if (cur.mode == M_VS) {
+          // ---- this wave's view of the entry
+          int mode;
+          if (!((cur.flags >> ih) & 1)) mode = M_SKIP;
+          else if (cur.kind == 1) mode = M_GATHER;
+          else if (it.kind == 1) {
+            const int aw_ = P0w / TK - cur.kt;
+            mode = (aw_ >= 1 && test_bit(fbits, aw_)) ? M_NONE : M_VS;
+          } else {
+            mode = (cur.kt * TK + TK - 1 > P0w) ? M_CAUSAL : M_NONE;
+          }
+          // 64-bit window of diagonal bits for this lane's row (bit b <-> offset lo + b)
+          uint64_t swin = 0;
+          if (mode == M_VS) {
             const int lo = iq - cur.kt * TK - 63;
             const int sh = lo & 31;
-            const uint64_t lo64 = ((uint64_t)mw.s1 << 32) | mw.s0;
-            const uint64_t hi64 = (uint64_t)mw.s2;
-            const uint64_t win = sh ? ((lo64 >> sh) | (hi64 << (64 - sh))) : lo64;   // bit b <-> offset lo + b
-            const uint64_t rev = ((uint64_t)__builtin_bitreverse32((uint32_t)win) << 32) |
-                                 __builtin_bitreverse32((uint32_t)(win >> 32));       // bit c <-> key c
-            M = (rev | (((uint64_t)mw.v1 << 32) | mw.v0)) & causal_mask64(iq - cur.kt * TK);
-          } else if (cur.mode == M_GATHER) {
-            // columns are ascending: keys c < n_le are <= iq
-            const int base = cur.kt * TK;
-            int lo2 = 0, hi2 = cur.cnt;
-            while (lo2 < hi2) {
-              const int mid = (lo2 + hi2) >> 1;
-              if (s_cols[base + mid] <= iq) lo2 = mid + 1; else hi2 = mid;
-            }
-            M = lo2 >= 64 ? ~0ull : ((1ull << lo2) - 1ull);
+            const uint64_t lo64 = ((uint64_t)ms1 << 32) | ms0;
+            swin = sh ? ((lo64 >> sh) | ((uint64_t)ms2 << (64 - sh))) : lo64;
           }
-          if (!row_ok) M = 0ull;
-          const bool masked = cur.mode != M_NONE;
-          bool act[2];
-          act[0] = live && __builtin_amdgcn_ballot_w64((uint32_t)M != 0u) != 0;
-          act[1] = live && __builtin_amdgcn_ballot_w64((uint32_t)(M >> 32) != 0u) != 0;
 
-          // ---- S^T = K Q^T
-          f32x16 sacc[2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-            if (act[kb]) {
-              const int row = 32 * kb + qn;
-#pragma unroll
-              for (int ks = 0; ks < 8; ++ks) {
-                const u32x4 x = *(const u32x4*)(s_k + row * 256 + swz_k(row, 2 * ks + hh) * 16);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf[ks], sacc[kb],
-                                                                   0, 0, 0);
+            // ---- mask over keys 32 kb .. +31 (bit c <-> key kt*64 + 32 kb + c)
+            const int ktop = iq - cur.kt * TK - 32 * kb;   // keys c <= ktop are causal
+            uint32_t M = ~0u;
+            if (mode == M_SKIP) {
+              M = 0u;
+            } else if (mode == M_CAUSAL) {
+              M = causal_mask32(ktop);
+            } else if (mode == M_VS) {
+              // key c of this half sits at window bit 63 - 32 kb - c
+              const uint32_t part = kb == 0 ? (uint32_t)(swin >> 32) : (uint32_t)swin;
+              M = (__builtin_bitreverse32(part) | (kb == 0 ? mv0 : mv1)) & causal_mask32(ktop);
+            } else if (mode == M_GATHER) {
+              const int base = cur.kt * TK + 32 * kb;
+              const int cnt = max(0, min(32, cur.cnt - 32 * kb));
+              int lo = 0, hi = cnt;
+              while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_cols[base + mid] <= iq) lo = mid + 1; else hi = mid;
               }
+              M = lo >= 32 ? ~0u : ((1u << lo) - 1u);
             }
-          }
-          // ---- mask and online softmax (scores kept raw; scale folded into exp2)
-          float mx = -INFINITY;
+            if (!row_ok) M = 0u;
+            const bool masked = mode != M_NONE;
+            if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) continue;
+
+            // ---- S^T = K Q^T for these 32 keys (eight K fragments read first)
+            f32x16 sacc;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (!act[kb]) continue;
-            const uint32_t mk = (uint32_t)(M >> (32 * kb)) >> (4 * hh);
+            for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+            const int row = 32 * kb + qn;
+            u32x4 kf[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(sk + row * 256 + swz_k(row, 2 * ks + hh) * 16);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+
+            // ---- mask, online softmax (raw scores; the scale is folded into exp2)
+            const uint32_t mk = M >> (4 * hh);
+            float mx = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              float x = sacc[kb][v];
-              if (masked && !((mk >> (8 * (v >> 2) + (v & 3))) & 1u)) x = -INFINITY;
-              sacc[kb][v] = x;
+              float x = sacc[v];
+              if (masked) {
+                const int pos = 8 * (v >> 2) + (v & 3);
+                const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
+                x = __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
+              }
+              sacc[v] = x;
               mx = fmaxf(mx, x);
             }
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
-          const bool grow = mx > m_run + 8.0f;
-          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float mnew = grow ? mx : m_run;
-            const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
-            l_run *= f;
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+            const bool grow = mx > m_run + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+              const float mnew = grow ? mx : m_run;
+              const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
+              l_run *= f;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+              for (int db = 0; db < 4; ++db)
 #pragma unroll
-              for (int v = 0; v < 16; ++v) acc[db][v] *= f;
-            m_run = mnew;
-          }
-          const float muse = (m_run == -INFINITY) ? 0.f : m_run;
-          uint32_t pk[2][8];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (!act[kb]) continue;
+                for (int v = 0; v < 16; ++v) acc[db][v] *= f;
+              m_run = mnew;
+            }
+            const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            uint32_t pk[8];
 #pragma unroll
             for (int v = 0; v < 16; v += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale2, -muse));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v + 1], scale2, -muse));
-              // normalise with the same bf16-rounded weights the PV product uses
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], scale2, -muse));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], scale2, -muse));
               const uint32_t pb = pack_bf16x2(p0, p1);
-              l_run += bf16_lo(pb) + bf16_hi(pb);
-              pk[kb][v >> 1] = pb;
+              // the row sum uses the same bf16-rounded weights as the PV product
+              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
+              pk[v >> 1] = pb;
             }
-          }
 
-          wait_vm();
-          __syncthreads();                       // V_n visible; every wave is done with K_n
-          Entry nxt;
-          nxt.mode = M_EMPTY;
-          if (n + 1 < c.nent) {
-            nxt = entry_of(c, n + 1, raw_next);
-            raw_next = entry_raw(c, n + 2);
-            if (nxt.mode != M_EMPTY) issue_tile<false>(kbp, a.Nk, nxt, s_cols, s_k, w, l);
-            issue_mask_loads(c, nxt, iq, row_ok, mw);
-          }
-
-          // ---- O^T += V^T P^T, keys 16 ks2 .. +15 per step
+            // ---- O^T += V^T P^T over these 32 keys (two 16-key steps)
 #pragma unroll
-          for (int ks2 = 0; ks2 < 4; ++ks2) {
-            const int kb = ks2 >> 1;
-            if (!act[kb]) continue;
-            const int o8 = (ks2 & 1) * 4;
-            u32x4 bx = {pk[kb][o8], pk[kb][o8 + 1], pk[kb][o8 + 2], pk[kb][o8 + 3]};
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
-            const int G = l >> 4, s = l & 15;
-            const int rowa = 16 * ks2 + 4 * (G >> 1) + (s >> 2);
-            const int rowb = rowa + 8;
+            for (int s2 = 0; s2 < 2; ++s2) {
+              u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
+              const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
+              const int rowa = 32 * kb + 16 * s2 + v_row0;
+              const int rowb = rowa + 8;
+              short4_t ya[4], yb[4];
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const int cch = 4 * db + 2 * (G & 1) + ((s & 3) >> 1);
-              const int half = (s & 1) * 8;
-              lds_short4_t* pa = (lds_short4_t*)((__attribute__((address_space(3))) char*)s_v + rowa * 256 +
-                                                 swz_v(rowa, cch) * 16 + half);
-              lds_short4_t* pb2 = (lds_short4_t*)((__attribute__((address_space(3))) char*)s_v + rowb * 256 +
-                                                  swz_v(rowb, cch) * 16 + half);
-              const short4_t ya = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa);
-              const short4_t yb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb2);
-              typedef short short8_t __attribute__((ext_vector_type(8)));
-              const short8_t ab = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
+              for (int db = 0; db < 4; ++db) {
+                const int cch = 4 * db + 2 * (G & 1) + ((si & 3) >> 1);
+                ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4_t*)(sv + rowa * 256 + swz_v(rowa, cch) * 16 + v_half));
+                yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4_t*)(sv + rowb * 256 + swz_v(rowb, cch) * 16 + v_half));
+              }
+#pragma unroll
+              for (int db = 0; db < 4; ++db) {
+                const short8_t ab = {ya[db][0], ya[db][1], ya[db][2], ya[db][3], yb[db][0], yb[db][1], yb[db][2], yb[db][3]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
+              }
+              __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
             }
           }
           cur = nxt;
+          have = have_n;
+          ms0 = ns0; ms1 = ns1; ms2 = ns2; mv0 = nv0; mv1 = nv1;
         }
-        if (!(c.kind == 1 && gcursor < gcount)) break;
+        if (!(it.kind == 1 && gcursor < gcount)) break;
+        __syncthreads();                         // the last tile's gathered columns are no longer read
       }
 
       // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       if (row_ok) {
-        const size_t obase = ((size_t)bh * a.Nq + qrow) * 128;
+        const size_t obase = ((size_t)it.bh * a.Nq + qrow) * 128;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -534,7 +618,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
             }
           }
         if (hh == 0 && a.lse) {
-          a.lse[(size_t)bh * a.Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+          a.lse[(size_t)it.bh * a.Nq + qrow] =
+              l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
         }
       }
     }
@@ -557,14 +642,14 @@ int cu_count() {
 
 struct VsLayout {
   int sw, vw, aw, acap, TA;
-  size_t off_s, off_v, off_a, off_f, off_al, off_ac, off_ctr, total_words;
+  size_t off_s, off_v, off_f, off_a2, off_ac, off_ctr, off_al, off_ale, total_words;
 };
 
 VsLayout vs_layout(int B, int H, int Nk) {
   VsLayout L;
   L.sw = (Nk + 31) / 32 + 5;
   L.vw = (Nk + 31) / 32 + 2;
-  L.TA = (Nk + TK - 1) / TK + 1;
+  L.TA = (Nk + TK - 1) / TK + 2;
   L.aw = (L.TA + 31) / 32 + 1;
   L.acap = L.TA;
   const size_t nbh = (size_t)B * H;
@@ -572,11 +657,12 @@ VsLayout vs_layout(int B, int H, int Nk) {
   L.off_ctr = off; off += 64;
   L.off_s = off; off += nbh * L.sw;
   L.off_v = off; off += nbh * L.vw;
-  L.off_a = off; off += nbh * L.aw;
   L.off_f = off; off += nbh * L.aw;
+  L.off_a2 = off; off += nbh * L.aw;
   L.off_ac = off; off += nbh;
   L.total_words = off;          // region zeroed before every call
   L.off_al = off; off += nbh * L.acap;
+  L.off_ale = off; off += nbh * L.acap;
   (void)off;
   return L;
 }
@@ -585,7 +671,7 @@ VsLayout vs_layout(int B, int H, int Nk) {
 
 size_t attn_workspace_bytes(int B, int H, int Nk) {
   VsLayout L = vs_layout(B, H, Nk);
-  return (L.off_al + (size_t)B * H * L.acap) * 4 + 256;
+  return (L.off_ale + (size_t)B * H * L.acap) * 4 + 256;
 }
 
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
@@ -597,15 +683,17 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
 
 hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   const int T = (a.Nq + TQ - 1) / TQ;
+  const int T2 = (T + 1) / 2;
   VsLayout L = vs_layout(a.B, a.H, a.Nk);
   uint32_t* base = (uint32_t*)ws;
   a.counters = (int32_t*)(base + L.off_ctr);
   a.sbits = base + L.off_s;
   a.vbits = base + L.off_v;
-  a.abits = base + L.off_a;
   a.fbits = base + L.off_f;
-  a.acount = (int32_t*)(base + L.off_ac);
-  a.alist = (int32_t*)(base + L.off_al);
+  a.a2bits = base + L.off_a2;
+  a.a2count = (int32_t*)(base + L.off_ac);
+  a.a2list = (int32_t*)(base + L.off_al);
+  a.a2le = (int32_t*)(base + L.off_ale);
   a.sw = L.sw; a.vw = L.vw; a.aw = L.aw; a.acap = L.acap;
 
   hipError_t e = launch_zero_u32(base, L.total_words, st);
@@ -640,7 +728,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   if (heads.empty()) return hipSuccess;
   std::stable_sort(heads.begin(), heads.end(), [](const HC& x, const HC& y) { return x.cost > y.cost; });
   Sched sc;
-  sc.T = T;
+  sc.T2 = T2;
   sc.nq = std::min<int>(kMaxQueues, (int)heads.size());
   std::vector<std::vector<int>> qh(sc.nq);
   std::vector<double> load(sc.nq, 0.0);
@@ -658,8 +746,8 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   }
   sc.qstart[sc.nq] = pos;
 
-  const long items = (long)heads.size() * T;
-  long grid = std::min<long>(items, (long)cu_count() * 4);
+  const long items = (long)heads.size() * T2;
+  long grid = std::min<long>(items, (long)cu_count() * 2);
   grid = std::max<long>(sc.nq, (grid / sc.nq) * sc.nq);
   hipLaunchKernelGGL(attn_kernel, dim3((unsigned)grid), dim3(NT), 0, st, a, sc);
   return hipGetLastError();

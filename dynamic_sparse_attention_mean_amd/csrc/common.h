@@ -28,8 +28,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two fp32 values to packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp64 -> bf16 bits with a single round-to-nearest-even step taken on the

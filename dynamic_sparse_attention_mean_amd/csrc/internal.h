@@ -69,9 +69,9 @@ struct AttnArgs {
   // Vertical-Slash sets and their compiled form (workspace)
   const int32_t* cols; const int32_t* cols_count; int cols_cap;
   const int32_t* diags; const int32_t* diags_count; int diags_cap;
-  uint32_t* sbits; uint32_t* vbits; uint32_t* abits; uint32_t* fbits;
-  int32_t* alist; int32_t* acount;
-  int sw, vw, aw, acap;              // words per head of each bitmap; alist capacity
+  uint32_t* sbits; uint32_t* vbits; uint32_t* abits; uint32_t* fbits; uint32_t* a2bits;
+  int32_t* a2list; int32_t* a2count; int32_t* a2le;   // A2 list, its size, #{a in A2 : a <= t}
+  int sw, vw, aw, acap;              // words per head of each bitmap; a2list capacity
   // Block sets
   const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
   // Token sets
