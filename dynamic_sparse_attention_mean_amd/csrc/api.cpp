@@ -264,10 +264,10 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 0 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
+  if (route_heads > 8) return fail(DSA_ERR_UNSUPPORTED, "route_heads > 8");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
   if (!out.idx || !out.count) return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
   if (out.cap < std::min(topk, shape->kv_len)) return fail(DSA_ERR_INVALID_ARG, "out.cap < topk");
-  if (!indexer_supported()) return fail(DSA_ERR_UNSUPPORTED, "the indexer is not built yet");
   const size_t need = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, n_idx_heads, route_heads)) + 256;
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   IndexerArgs a;
@@ -311,7 +311,7 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   }
   if (use[DSA_PATTERN_TOKEN]) {
     if (!tok || !tok->idx || !tok->count || tok->cap < 1) return fail(DSA_ERR_INVALID_ARG, "token heads need a token index set");
-    if (!attn_token_supported()) return fail(DSA_ERR_UNSUPPORTED, "token heads are not built yet");
+    if (tok->cap > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "more than %d tokens per query", kMaxTokensPerQuery);
   }
   const size_t need = ws_attn(shape);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

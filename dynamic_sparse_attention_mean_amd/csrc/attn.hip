@@ -725,6 +725,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
       else per = std::min<double>(0.5 * a.Nk / TK, 2.0 * a.diags_cap / TK + 1 + a.cols_cap / (double)TK);
       heads.push_back({per * T, b * a.H + h});
     }
+  if ((e = launch_token_attention(a, st)) != hipSuccess) return e;
   if (heads.empty()) return hipSuccess;
   std::stable_sort(heads.begin(), heads.end(), [](const HC& x, const HC& y) { return x.cost > y.cost; });
   Sched sc;

@@ -1,13 +1,425 @@
-// Indexer token top-k (placeholder until the indexer kernels land).
+// Indexer token top-k (DSA) and its routed variant (MISA), plus attention over
+// per-query token lists.
+//
+// "MISA" (gist.science 2605.07363), section on the problem: the DeepSeek sparse
+// attention indexer scores every key with 64 light heads and keeps the best
+// tokens, and the main attention reads only those.  Section on how MISA works:
+// a router looks at the keys in large blocks, picks 8 of the 64 heads for each
+// query, and only those heads score tokens.
+//
+//   score[i, j] = sum_{h in H(i)} w[i, h] * max(0, q_idx[i, h] . k_idx[j])   (j <= p_i)
+//   router:  r[i, h] = w[i, h] * max(0, max_J q_idx[i, h] . Kbar_J), complete blocks J
+//   tokens:  top-k of score[i, :], ties to the lower index, ascending
+//
+// Kernels (gfx950):
+//   qk_heads_kernel<MODE>: (query, head) rows x keys on v_mfma_f32_32x32x16_bf16.
+//     The rows of a wave are one query's 64 heads (dense indexer, router) or four
+//     queries' routed heads (routed indexer); keys stream through a two-stage LDS
+//     ring (DMA).  Epilogues: ReLU * w summed over heads (indexer) or a running
+//     max over blocks (router).  The MFMA output layout puts 16 heads of one key
+//     in a lane, so the head sum is 16 in-lane FMAs plus one lane swap.
+//   router_select_kernel: top-r heads per query (rank counting over 64 values).
+//   token_select_kernel: radix top-k per query row (select.h).
+//   token_attn_kernel: per (query, head) softmax over the gathered token list on
+//     VALU; the grid is head-major so a head's K/V stays in the Infinity Cache.
 #include "common.h"
 #include "internal.h"
+#include "select.h"
+
+#include <algorithm>
 
 namespace dsa {
-bool indexer_supported() { return false; }
-bool attn_token_supported() { return false; }
-size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads) {
-  (void)Hi; (void)route_heads;
-  return (size_t)Nq * Nk * 4;
+namespace {
+
+constexpr int KT = 64;            // keys per tile
+constexpr int NW = 8;             // waves per workgroup
+constexpr int NTI = NW * 64;      // threads per workgroup
+
+enum { MODE_DENSE = 0, MODE_ROUTED = 1, MODE_ROUTER = 2 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
-hipError_t launch_indexer(const IndexerArgs&, void*, hipStream_t) { return hipErrorNotSupported; }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
+
+struct QkArgs {
+  const uint16_t* q_idx;     // [Nq, Hi, 128]
+  const uint16_t* keys;      // [nkeys, 128] (k_idx, or block means for the router)
+  const float* w;            // [Nq, Hi]
+  const int32_t* route;      // [Nq, R] routed heads (MODE_ROUTED)
+  float* out;                // MODE_DENSE / ROUTED: scores [Nq, Nk]; MODE_ROUTER: r [Nq, Hi]
+  int Nq, Nk, Hi, R, q_offset, nkeys, block;
+};
+
+// Queries of this workgroup: MODE_DENSE / ROUTER -> 8 (one per wave), MODE_ROUTED -> 32 (four per wave).
+template <int MODE>
+__global__ __launch_bounds__(NTI) void qk_heads_kernel(const QkArgs a) {
+  __shared__ __align__(1024) char s_k[2][KT * 256];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, qn = l & 31, hh = l >> 5;
+  constexpr int QPW = MODE == MODE_ROUTED ? 4 : 1;     // queries per wave
+  constexpr int NB = MODE == MODE_ROUTED ? 1 : 2;      // 32-row blocks per wave
+  const int q0 = (blockIdx.x * NW + w) * QPW;          // first query of this wave
+
+  // ---- A operand: the wave's (query, head) rows, kept in registers
+  //   block hb, row m = l & 31 -> (query, head); lane holds d = 16 ks + 8 hh .. +7
+  bf16x8 af[NB][8];
+  float wv[NB][16];                                    // w of the 16 rows this lane's outputs cover
+  bool rows_ok[NB];
+#pragma unroll
+  for (int hb = 0; hb < NB; ++hb) {
+    int qq, head;
+    if (MODE == MODE_ROUTED) {
+      qq = q0 + (qn >> 3);
+      const int slot = qn & 7;
+      head = (qq < a.Nq && slot < a.R) ? a.route[(size_t)qq * a.R + slot] : -1;
+    } else {
+      qq = q0;
+      head = 32 * hb + qn;
+      if (head >= a.Hi) head = -1;
+    }
+    const bool ok = qq < a.Nq && head >= 0;
+    rows_ok[hb] = ok;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *(const u32x4*)(a.q_idx + ((size_t)qq * a.Hi + head) * 128 + 16 * ks + 8 * hh);
+      af[hb][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    // output rows of value v: m = 8 (v >> 2) + 4 hh + (v & 3)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * hh + (v & 3);
+      int q2, h2;
+      if (MODE == MODE_ROUTED) {
+        q2 = q0 + (m >> 3);
+        const int slot = m & 7;
+        h2 = (q2 < a.Nq && slot < a.R) ? a.route[(size_t)q2 * a.R + slot] : -1;
+      } else {
+        q2 = q0;
+        h2 = 32 * hb + m;
+        if (h2 >= a.Hi) h2 = -1;
+      }
+      wv[hb][v] = (q2 < a.Nq && h2 >= 0) ? a.w[(size_t)q2 * a.Hi + h2] : 0.f;
+    }
+  }
+  (void)rows_ok;
+
+  // keys each query may see: j <= p_q (indexer) or complete blocks (router)
+  int last_key;   // last key (tile row index into a.keys) any query of the workgroup needs
+  {
+    const int qmax = min(a.Nq - 1, (blockIdx.x * NW + NW) * QPW - 1);
+    const int pmax = qmax + a.q_offset;
+    last_key = MODE == MODE_ROUTER ? ((pmax + 1) / a.block - 1) : pmax;
+    last_key = min(last_key, a.nkeys - 1);
+  }
+  const int ntiles = last_key >= 0 ? last_key / KT + 1 : 0;
+
+  // this lane's limits: query of each output value
+  float rmax[NB][16];
+#pragma unroll
+  for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rmax[hb][v] = -INFINITY;
+
+  // DMA of a 16 KB key tile: wave w, instruction j fills LDS block 8 j + w,
+  // i.e. rows 4 (8 j + w) + lane / 16
+  auto issue = [&](int tile, int stage) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int blk = 8 * j + w;
+      const int r = 4 * blk + (l >> 4);
+      const int key = min(tile * KT + r, a.nkeys - 1);
+      const int c = swz(r, l & 15);
+      dma16(a.keys + (size_t)key * 128 + c * 8, (lds_void_t*)(s_k[stage] + blk * 1024));
+    }
+  };
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    wait_vm();
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, stage ^ 1);
+    const char* sk = s_k[stage];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * kb + qn;
+      u32x4 kf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(sk + row * 256 + swz(row, 2 * ks + hh) * 16);
+      f32x16 c[NB];
+#pragma unroll
+      for (int hb = 0; hb < NB; ++hb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[hb][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          c[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[hb][ks], __builtin_bit_cast(bf16x8, kf[ks]), c[hb], 0, 0, 0);
+      }
+      const int key = t * KT + 32 * kb + qn;           // key of this lane's output column
+      if (MODE == MODE_ROUTER) {
+        // complete block `key` (J) is visible to query q iff 64 J + 63 <= p_q
+        const int p = q0 + a.q_offset;
+        const bool vis = key <= last_key && (key + 1) * a.block - 1 <= p;
+#pragma unroll
+        for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (vis) rmax[hb][v] = fmaxf(rmax[hb][v], c[hb][v]);
+      } else {
+        float s[QPW];
+#pragma unroll
+        for (int j = 0; j < QPW; ++j) s[j] = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int j = MODE == MODE_ROUTED ? (v >> 2) : 0;   // query of row 8 (v >> 2) + ...
+            s[j] = __builtin_fmaf(wv[hb][v], fmaxf(c[hb][v], 0.f), s[j]);
+          }
+#pragma unroll
+        for (int j = 0; j < QPW; ++j) {
+          const float tot = s[j] + __shfl_xor(s[j], 32, 64);
+          const int qq = q0 + j;
+          if (hh == (j & 1) && qq < a.Nq && key <= qq + a.q_offset && key < a.Nk)
+            a.out[(size_t)qq * a.Nk + key] = tot;
+        }
+      }
+    }
+  }
+  if (MODE == MODE_ROUTER) {
+    // max over the lanes of each head (the 32 key columns), then r = w * max(0, .)
+#pragma unroll
+    for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = rmax[hb][v];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+        rmax[hb][v] = x;
+      }
+    if (qn == 0 && q0 < a.Nq) {
+#pragma unroll
+      for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int h = 32 * hb + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (h < a.Hi) {
+            const float mx = rmax[hb][v];
+            a.out[(size_t)q0 * a.Hi + h] = wv[hb][v] * (mx > 0.f ? mx : 0.f);
+          }
+        }
+    }
+  }
+}
+
+// Top-R heads per query by r (ties to the lower head), ascending head order.
+__global__ void router_select_kernel(const float* r, int Nq, int Hi, int R, int32_t* route, int32_t* route_out) {
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (q >= Nq) return;
+  const float x = l < Hi ? r[(size_t)q * Hi + l] : -INFINITY;
+  int rank = 0;
+  for (int o = 0; o < Hi; ++o) {
+    const float y = __shfl(x, o, 64);
+    rank += (y > x) || (y == x && o < l);
+  }
+  const bool sel = l < Hi && rank < R;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(sel);
+  if (sel) {
+    const uint32_t pos = ballot_rank(bal);
+    route[(size_t)q * R + pos] = l;
+    if (route_out) route_out[(size_t)q * R + pos] = l;
+  }
+}
+
+// Top-k per query row over keys [0, p_q].
+__global__ __launch_bounds__(1024) void token_select_kernel(const float* scores, int Nq, int Nk, int q_offset, int k,
+                                                            int32_t* tok, int32_t* cnt, int cap) {
+  __shared__ SelectSmem<1024> sm;
+  const int q = blockIdx.x;
+  const int p = q + q_offset;
+  const int n = select_topk<1024>(scores + (size_t)q * Nk, 0, min(p + 1, Nk), -1, -1, k, tok + (size_t)q * cap, sm);
+  if (threadIdx.x == 0) cnt[q] = n;
+}
+
+// ---------------------------------------------------------------- token attention
+constexpr int TA_THREADS = 256;
+constexpr int TA_MAXTOK = 4096;
+
+// One workgroup per (head, query); heads outermost so a head's K/V stay cached.
+__global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                                                int H, int Hkv, int Nq, int Nk, const int32_t* tidx,
+                                                                const int32_t* tcount, int tcap, void* o, float* lse,
+                                                                int out_f32, int B, HeadList th) {
+  __shared__ float s_p[TA_MAXTOK];
+  __shared__ int32_t s_t[TA_MAXTOK];
+  __shared__ float s_red[4][128];
+  __shared__ float s_ms[8];
+  const int bid = blockIdx.x;
+  const int h = th.h[bid / (Nq * B)];
+  const int rem = bid % (Nq * B);
+  const int b = rem / Nq, i = rem % Nq;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int n = min(min(tcount[(size_t)b * Nq + i], tcap), TA_MAXTOK);
+  const int32_t* tl = tidx + ((size_t)b * Nq + i) * tcap;
+  for (int x = tid; x < n; x += TA_THREADS) {
+    const int j = tl[x];
+    s_t[x] = (j >= 0 && j < Nk) ? j : -1;
+  }
+  __syncthreads();
+  const uint16_t* qrow = q + (((size_t)b * H + h) * Nq + i) * 128;
+  const uint16_t* kb = k + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
+  const uint16_t* vb = v + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
+  // scores: 16 lanes per token (8 dims each), 4 tokens per wave step
+  const int sub = l & 15, tg = l >> 4;
+  const u32x4 qx = *(const u32x4*)(qrow + sub * 8);
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { qv[2 * e] = bf16_lo(qx[e]); qv[2 * e + 1] = bf16_hi(qx[e]); }
+  const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
+  float mloc = -INFINITY;
+  for (int x0 = wv * 4; x0 < n; x0 += 16) {
+    const int x = x0 + tg;
+    float d = 0.f;
+    int j = -1;
+    if (x < n) j = s_t[x];
+    if (j >= 0) {
+      const u32x4 kx = *(const u32x4*)(kb + (size_t)j * 128 + sub * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = __builtin_fmaf(qv[2 * e], bf16_lo(kx[e]), d);
+        d = __builtin_fmaf(qv[2 * e + 1], bf16_hi(kx[e]), d);
+      }
+    }
+#pragma unroll
+    for (int o2 = 8; o2 >= 1; o2 >>= 1) d += __shfl_xor(d, o2, 64);
+    if (x < n && sub == 0) {
+      const float s = j >= 0 ? d * scale : -INFINITY;
+      s_p[x] = s;
+      mloc = fmaxf(mloc, s);
+    }
+  }
+  mloc = wave_max(mloc);
+  if (l == 0) s_ms[wv] = mloc;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(s_ms[0], s_ms[1]), fmaxf(s_ms[2], s_ms[3]));
+  float lsum = 0.f;
+  for (int x = tid; x < n; x += TA_THREADS) {
+    const float p = (m == -INFINITY) ? 0.f : __expf(s_p[x] - m);
+    s_p[x] = p;
+    lsum += p;
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if (l == 0) s_ms[4 + wv] = lsum;
+  // O: lane l owns dims 2l, 2l+1; wave wv walks tokens wv, wv+4, ...
+  float o0 = 0.f, o1 = 0.f;
+  for (int x = wv; x < n; x += 4) {
+    const int j = s_t[x];
+    if (j < 0) continue;
+    const float p = s_p[x];
+    const uint32_t vx = *(const uint32_t*)(vb + (size_t)j * 128 + 2 * l);
+    o0 = __builtin_fmaf(p, bf16_lo(vx), o0);
+    o1 = __builtin_fmaf(p, bf16_hi(vx), o1);
+  }
+  s_red[wv][2 * l] = o0;
+  s_red[wv][2 * l + 1] = o1;
+  __syncthreads();
+  if (tid < 128) {
+    const float ltot = s_ms[4] + s_ms[5] + s_ms[6] + s_ms[7];
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float val = (s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]) * inv;
+    const size_t oi = (((size_t)b * H + h) * Nq + i) * 128 + tid;
+    if (out_f32) ((float*)o)[oi] = val;
+    else ((uint16_t*)o)[oi] = (uint16_t)f32_to_bf16_bits(val);
+    if (tid == 0 && lse) lse[((size_t)b * H + h) * Nq + i] = ltot > 0.f ? m + __logf(ltot) : -INFINITY;
+  }
+}
+
+struct IdxLayout {
+  size_t off_scores, off_kbar, off_r, off_route, total;
+};
+IdxLayout idx_layout(int Nq, int Nk, int Hi, int R) {
+  IdxLayout L;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  L.off_scores = off; off = al(off + (size_t)Nq * Nk * 4);
+  L.off_kbar = off; off = al(off + (size_t)((Nk + 63) / 64) * 128 * 2);
+  L.off_r = off; off = al(off + (size_t)Nq * Hi * 4);
+  L.off_route = off; off = al(off + (size_t)Nq * std::max(R, 1) * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads) {
+  return idx_layout(Nq, Nk, Hi, route_heads).total;
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
+  if (a.route_heads > 8) return hipErrorNotSupported;
+  IdxLayout L = idx_layout(a.Nq, a.Nk, a.Hi, a.route_heads);
+  char* base = (char*)ws;
+  float* scores = (float*)(base + L.off_scores);
+  QkArgs q;
+  q.q_idx = a.q_idx;
+  q.w = a.w;
+  q.Nq = a.Nq; q.Nk = a.Nk; q.Hi = a.Hi; q.q_offset = a.q_offset;
+  q.block = 64;
+  if (a.route_heads > 0) {
+    // router: block means of the indexer keys, head scores, top-R heads
+    uint16_t* kbar = (uint16_t*)(base + L.off_kbar);
+    float* r = (float*)(base + L.off_r);
+    int32_t* route = (int32_t*)(base + L.off_route);
+    HeadList one;
+    one.n = 1;
+    one.h[0] = 0;
+    hipError_t e = launch_pool(a.k_idx, 1, 1, a.Nk, one, 64, kbar, st);
+    if (e != hipSuccess) return e;
+    q.keys = kbar;
+    q.nkeys = (a.Nk + 63) / 64;
+    q.out = r;
+    q.route = nullptr;
+    q.R = 0;
+    hipLaunchKernelGGL(qk_heads_kernel<MODE_ROUTER>, dim3((a.Nq + NW - 1) / NW), dim3(NTI), 0, st, q);
+    hipLaunchKernelGGL(router_select_kernel, dim3((a.Nq + 3) / 4), dim3(256), 0, st, r, a.Nq, a.Hi, a.route_heads,
+                       route, a.route);
+    q.keys = a.k_idx;
+    q.nkeys = a.Nk;
+    q.out = scores;
+    q.route = route;
+    q.R = a.route_heads;
+    hipLaunchKernelGGL(qk_heads_kernel<MODE_ROUTED>, dim3((a.Nq + 4 * NW - 1) / (4 * NW)), dim3(NTI), 0, st, q);
+  } else {
+    q.keys = a.k_idx;
+    q.nkeys = a.Nk;
+    q.out = scores;
+    q.route = nullptr;
+    q.R = 0;
+    hipLaunchKernelGGL(qk_heads_kernel<MODE_DENSE>, dim3((a.Nq + NW - 1) / NW), dim3(NTI), 0, st, q);
+  }
+  hipLaunchKernelGGL(token_select_kernel, dim3(a.Nq), dim3(1024), 0, st, scores, a.Nq, a.Nk, a.q_offset, a.topk, a.tok,
+                     a.tok_count, a.tok_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.tcap > TA_MAXTOK) return hipErrorNotSupported;
+  HeadList th;
+  th.n = 0;
+  for (int h = 0; h < a.H; ++h)
+    if (a.kind[h] == 3) th.h[th.n++] = h;
+  if (th.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(token_attn_kernel, dim3((unsigned)((size_t)th.n * a.B * a.Nq)), dim3(TA_THREADS), 0, st, a.q,
+                     a.k, a.v, a.H, a.Hkv, a.Nq, a.Nk, a.tidx, a.tcount, a.tcap, a.o, a.lse, a.out_f32, a.B, th);
+  return hipGetLastError();
+}
+
 }  // namespace dsa

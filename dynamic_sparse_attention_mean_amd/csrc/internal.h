@@ -91,10 +91,11 @@ struct IndexerArgs {
   int32_t* tok; int32_t* tok_count; int tok_cap;
   int32_t* route;          // nullable [Nq, route_heads]
 };
-bool indexer_supported();
-bool attn_token_supported();
 size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads);
 hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st);
+constexpr int kMaxTokensPerQuery = 4096;
+// Attention of the TOKEN heads over per-query token lists.
+hipError_t launch_token_attention(const AttnArgs& a, hipStream_t st);
 
 // zero n int32 words (used instead of hipMemsetAsync so the sequence stays
 // capturable into a graph)

@@ -1,0 +1,88 @@
+"""GPU parity of the indexer token top-k (dense and routed) and of attention
+over per-query token lists, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import dynamic_sparse_attention_mean_amd as dsa
+
+from parity import assert_attention_close, assert_set_matches, band_topk, f64
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def small_chunk(seed, N, Nq, Hi, topk, H=4):
+    return synth.indexer_chunk(seed=seed, N=N, Nq=Nq, Hi=Hi, H=H, topk=topk)
+
+
+@pytest.mark.parametrize("N,Nq,Hi,topk,route", [(1000, 70, 64, 50, 0), (777, 33, 16, 700, 0),
+                                                (1500, 90, 64, 64, 8), (640, 64, 12, 100, 3)])
+def test_indexer_token_sets(N, Nq, Hi, topk, route):
+    w = small_chunk(11 + N, N, Nq, Hi, topk)
+    qi, ki, wt = w.extra["q_idx"], w.extra["k_idx"], w.extra["w"]
+    out = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+    rt = torch.full((Nq, max(route, 1)), -1, dtype=torch.int32, device=DEV)
+    dsa.build_index_tokens(qi.to(DEV), ki.to(DEV), wt.to(DEV), topk, out, route_heads=route,
+                           route=rt if route else None)
+    torch.cuda.synchronize()
+    qo = N - Nq
+    qf, kf, wf = f64(qi), f64(ki), wt.double().numpy()
+    heads = None
+    if route:
+        # the GPU's routing decision, checked against the oracle router within the band
+        gr = rt.cpu().numpy()
+        kbar = O.block_means(kf, 64)
+        for i in range(Nq):
+            p = i + qo
+            nc = (p + 1) // 64
+            best = (kbar[:nc] @ qf[i].T).max(axis=0) if nc else np.zeros(Hi)
+            r = wf[i] * np.maximum(best, 0.0)
+            sel, c, tol = band_topk(r, np.arange(Hi), route)
+            assert_set_matches(gr[i], r, sel, c, tol, expect_count=route, what=f"route q{i}")
+        heads = gr
+    for i in range(Nq):
+        p = i + qo
+        sc = O.indexer_row(qf[i], kf, wf[i], p, None if heads is None else heads[i])
+        full = np.full(N, -np.inf)
+        full[:p + 1] = sc
+        sel, c, tol = band_topk(full, np.arange(p + 1), topk)
+        n = int(out.count[0, i].item())
+        assert_set_matches(out.idx[0, i, :n].cpu().numpy(), full, sel, c, tol, expect_count=min(topk, p + 1),
+                           what=f"tokens q{i}")
+
+
+@pytest.mark.parametrize("N,Nq,k", [(1000, 70, 50), (300, 300, 40), (513, 17, 600)])
+def test_token_attention_on_oracle_sets(N, Nq, k):
+    H = 4
+    g = np.random.default_rng(N)
+    q, kk, v = synth.random_qkv(N + 1, 1, H, H, N, Nq=Nq)
+    qo = N - Nq
+    tok = [np.sort(g.choice(i + qo + 1, min(k, i + qo + 1), replace=False)) for i in range(Nq)]
+    ti = dsa.TokenIndex.empty(1, Nq, k, DEV)
+    idx = ti.idx.cpu()
+    for i, t in enumerate(tok):
+        idx[0, i, :len(t)] = torch.from_numpy(t.astype(np.int32))
+    ti.idx.copy_(idx)
+    ti.count.copy_(torch.tensor([[len(t) for t in tok]], dtype=torch.int32))
+    o, lse = dsa.sparse_prefill_attn(q.to(DEV), kk.to(DEV), v.to(DEV), [dsa.TOKEN] * H, tok=ti)
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref_o, ref_l = O.attention_rows(f64(q[0, h]), f64(kk[0, h]), f64(v[0, h]), list(range(Nq)), tok)
+        assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l, f"token head {h}")
+
+
+def test_indexer_pipeline_end_to_end():
+    # GPU-built token sets feed the token attention; outputs match the oracle on those sets
+    N, Nq, Hi, topk, H = 1200, 80, 64, 96, 4
+    w = small_chunk(5, N, Nq, Hi, topk, H=H)
+    out = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+    dsa.build_index_tokens(w.extra["q_idx"].to(DEV), w.extra["k_idx"].to(DEV), w.extra["w"].to(DEV), topk, out)
+    o, lse = dsa.sparse_prefill_attn(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), [dsa.TOKEN] * H, tok=out)
+    torch.cuda.synchronize()
+    sets = [out.idx[0, i, :out.count[0, i]].cpu().numpy() for i in range(Nq)]
+    for h in range(H):
+        ref_o, ref_l = O.attention_rows(f64(w.q[0, h]), f64(w.k[0, h]), f64(w.v[0, h]), list(range(Nq)), sets)
+        assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l, f"pipeline head {h}")
