@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark of one dynamic sparse prefill attention layer on one MI355X.
+"""Benchmark of dynamic sparse prefill attention on one MI355X.
 
-A step is one pass of the whole hot path over the mixed-pattern 128K layer
-(32 Q / 8 KV heads, d = 128, N = 131072, bf16): A-shape sets for heads 0-10,
-Vertical-Slash scoring + selection for heads 11-26, mean-pooled block top-128
-for heads 27-31, then sparse attention over all 32 heads.  Inputs are seeded and
-synthetic and already resident in HBM when the timed region starts.
+Default workload (the headline): one attention layer at N = 131072 with mixed
+per-head patterns (32 Q / 8 KV heads, d = 128, bf16): A-shape sets for heads
+0-10, Vertical-Slash scoring + selection for heads 11-26, mean-pooled block
+top-128 for heads 27-31, then sparse attention over all 32 heads.  A step is
+that whole pass (index build + attention) over inputs already resident in HBM.
 
-Prints one JSON line (see the design doc for the fields).
+Other workloads (--workload) measure the remaining settings with the same
+protocol; they are reported alongside, the headline line is the default.
+
+Prints one JSON line (fields described in the design doc).
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,19 +33,39 @@ from dynamic_sparse_attention_mean_amd.pipeline import SparsePrefillLayer  # noq
 METRIC = "ms per attn layer (index build + sparse attn) at 128K; effective TFLOP/s"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "dynamic_sparse_attention_mean_amd", "csrc")
+# sources the attention kernel is compiled from: a counter record holds only while these are unchanged
+ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attn.hip", "common.h", "internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_mixed128k_traffic.json")
+
+WORKLOADS = {
+    "mixed128k": ("mixed-pattern layer, 32 Q / 8 KV heads, d=128, N=131072: heads 0-10 A-shape (sink 128, local "
+                  "2048), 11-26 Vertical-Slash (last_q 64, 1000 cols, 4096 diags), 27-31 block top-128 of 64",
+                  lambda: synth.config(3)),
+    "vs4k": ("one Vertical-Slash head, N=4096, last_q 64, 256 cols + 256 diags", lambda: synth.config(1)),
+    "block32k-topk": ("8 block heads, N=32768, block 64, top-16 + first + diagonal", lambda: synth.config(2)),
+    "block32k-thresh": ("8 block heads, N=32768, block 64, threshold max - ln 20 + first + diagonal",
+                        lambda: synth.config(2, mode="thresh")),
+    "thresh4k": ("32 Q / 8 KV heads, N=4096, block 128, threshold max - ln 20", lambda: synth.config(4, N=4096)),
+    "thresh256k": ("32 Q / 8 KV heads, N=262144, block 128, threshold max - ln 20",
+                   lambda: synth.config(4, N=262144)),
+    "indexer128k": ("indexer top-2048 over N=131072 for an 8192-query chunk (64 heads, dense) + token attention "
+                    "(16 heads)", lambda: synth.config(5)),
+    "indexer128k-routed": ("indexer top-2048 over N=131072, 8 of 64 heads routed per query + token attention "
+                           "(16 heads)", lambda: synth.config(5, route_heads=8)),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def selected_count(layer, w):
+def selected_count_layer(layer, w):
     """Exact sum_h sum_i |M_h(i)| of the layer's index sets (read back from the device)."""
     B, H, Hkv, Nq, Nk, d = w.shape
     pos = torch.arange(Nq, dtype=torch.int64) + w.q_offset
     total = 0
-    vsi = layer.vs_index
-    bi = layer.blk_index
+    vsi, bi = layer.vs_index, layer.blk_index
     for b in range(B):
         for h in range(H):
             kind = layer.kinds[h]
@@ -66,72 +90,152 @@ def selected_count(layer, w):
                     if r1 <= r0:
                         continue
                     J = idx[I, :int(cnt[I])].long()
-                    full = int((J < I).sum()) * block * (r1 - r0)
-                    diag = int((J == I).sum()) * ((r1 - r0) * (r1 - r0 + 1) // 2)
-                    total += full + diag
+                    total += int((J < I).sum()) * block * (r1 - r0)
+                    total += int((J == I).sum()) * ((r1 - r0) * (r1 - r0 + 1) // 2)
     return total
 
 
-def cpu_baseline(w, layer, sample_rows=64, seed=0):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to the layer."""
-    import oracle as O
-    from oracle.bf16 import to_f64
+def _oracle_threads():
     threads = torch.get_num_threads()
     try:
         from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [threads])
     except Exception:
         pass
+    return threads
+
+
+def cpu_baseline(w, sample_rows=192, seed=0):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to the
+    layer.  Every index set is the oracle's own (index rules timed in full for
+    every head); attention is timed on `sample_rows` random rows per head and
+    scaled to all rows."""
+    import oracle as O
+    from oracle.bf16 import to_f64
     B, H, Hkv, Nq, Nk, d = w.shape
     rng = np.random.default_rng(seed)
-    t_index = 0.0
-    # one head of each dynamic rule, timed, scaled by the number of such heads
-    n_vs = sum(1 for p in w.heads if p.kind == dsa.VS and not p.ashape)
-    n_blk = sum(1 for p in w.heads if p.kind == dsa.BLOCK)
-    sets = {}
+    t_index = t_attn = 0.0
     for h, p in enumerate(w.heads):
         kvh = h // (H // Hkv)
-        if p.kind == dsa.VS and not p.ashape and "vs" not in sets:
-            t0 = time.perf_counter()
-            v, s = O.vs_scores(to_f64(w.q[0, h, Nq - p.last_q:]), to_f64(w.k[0, kvh]))
-            O.vs_select(v, s, p.nv, p.ns)
-            t_index += (time.perf_counter() - t0) * n_vs
-            sets["vs"] = 1
-        if p.kind == dsa.BLOCK and "blk" not in sets:
-            t0 = time.perf_counter()
-            S = O.block_scores(O.block_means(to_f64(w.q[0, h]), p.block), O.block_means(to_f64(w.k[0, kvh]), p.block))
-            O.select_blocks(S, p.mode, k=p.topk)
-            t_index += (time.perf_counter() - t0) * n_blk
-            sets["blk"] = 1
-    # attention: `sample_rows` random rows per head on the layer's own index sets
-    t_attn = 0.0
-    flops_sample = 0
-    vsi, bi = layer.vs_index, layer.blk_index
-    for h in range(H):
-        kvh = h // (H // Hkv)
+        kf = None
+        t0 = time.perf_counter()
+        if p.kind == dsa.VS and p.ashape:
+            V, S = O.ashape_sets(Nk, p.sink, p.local)
+        elif p.kind == dsa.VS:
+            kf = to_f64(w.k[0, kvh])
+            v, s = O.vs_scores(to_f64(w.q[0, h, Nq - p.last_q:]), kf)
+            V, S = O.vs_select(v, s, p.nv, p.ns)
+        elif p.kind == dsa.BLOCK:
+            kf = to_f64(w.k[0, kvh])
+            S_ = O.block_scores(O.block_means(to_f64(w.q[0, h]), p.block), O.block_means(kf, p.block))
+            sel = O.select_blocks(S_, p.mode, k=p.topk, log_alpha=p.log_alpha, force_first=p.force_first,
+                                  force_diag=p.force_diag)
+        t_index += time.perf_counter() - t0
         rows = np.sort(rng.choice(Nq, sample_rows, replace=False))
-        if layer.kinds[h] == dsa.VS:
-            V = vsi.cols[0, h, :int(vsi.cols_count[0, h])].cpu().numpy()
-            S = vsi.diags[0, h, :int(vsi.diags_count[0, h])].cpu().numpy()
-            rs = [O.row_set_vs(int(i), V, S) for i in rows]
-        elif layer.kinds[h] == dsa.BLOCK:
-            sel = [bi.idx[0, h, I, :int(bi.count[0, h, I])].cpu().numpy() for I in range(bi.idx.shape[2])]
-            rs = [O.row_set_block(int(i), sel, bi.block, Nk) for i in rows]
+        if p.kind == dsa.VS:
+            rs = [O.row_set_vs(int(i) + w.q_offset, V, S) for i in rows]
+        elif p.kind == dsa.BLOCK:
+            rs = [O.row_set_block(int(i), sel, p.block, Nk) for i in rows]
         else:
-            rs = [O.row_set_dense(int(i)) for i in rows]
-        need = np.unique(np.concatenate(rs))
-        kk = np.zeros((Nk, d))
-        vv = np.zeros((Nk, d))
-        kk[need] = to_f64(w.k[0, kvh][torch.from_numpy(need)])
-        vv[need] = to_f64(w.v[0, kvh][torch.from_numpy(need)])
+            rs = [O.row_set_dense(int(i) + w.q_offset) for i in rows]
+        kf = to_f64(w.k[0, kvh]) if kf is None else kf
+        vf = to_f64(w.v[0, kvh])
         q = to_f64(w.q[0, h][torch.from_numpy(rows)])
         t0 = time.perf_counter()
-        O.attention_rows(q, kk, vv, list(range(len(rows))), rs)
+        O.attention_rows(q, kf, vf, list(range(len(rows))), rs)
         t_attn += time.perf_counter() - t0
-        flops_sample += 4 * d * sum(len(r) for r in rs)
-    t_attn_layer = t_attn * (Nq / sample_rows)
-    return dict(t_index=t_index, t_attn_layer=t_attn_layer, t_attn_sample=t_attn, flops_sample=flops_sample,
-                threads=threads, sample_rows=sample_rows)
+    return dict(t_index=t_index, t_attn_layer=t_attn * (Nq / sample_rows), t_attn_sample=t_attn,
+                threads=_oracle_threads(), sample=f"index rules of all {H} heads in full; attention on "
+                f"{sample_rows} random rows per head, scaled to {Nq} rows")
+
+
+def cpu_baseline_indexer(w, sample_queries=32, seed=0):
+    """The fp64 oracle indexer (router, scores, top-k) and token attention on a
+    few sampled queries of the chunk, scaled to the chunk."""
+    import oracle as O
+    from oracle.bf16 import to_f64
+    B, H, Hkv, Nq, Nk, d = w.shape
+    qi, ki, wt = w.extra["q_idx"], w.extra["k_idx"], w.extra["w"]
+    topk, route = w.extra["topk"], w.extra["route_heads"]
+    rows = np.sort(np.random.default_rng(seed).choice(Nq, sample_queries, replace=False))
+    kf = to_f64(ki)
+    t_index = t_attn = 0.0
+    sets = []
+    for i in rows:
+        p = int(i) + w.q_offset
+        t0 = time.perf_counter()
+        heads = None
+        if route:
+            heads = O.router_heads(to_f64(qi[i:i + 1]), kf, wt[i:i + 1].double().numpy(), p, route_heads=route)[0]
+        sc = O.indexer_row(to_f64(qi[i]), kf, wt[i].double().numpy(), p, heads)
+        sets.append(O.token_topk(sc, p, topk))
+        t_index += time.perf_counter() - t0
+    for h in range(H):
+        kk = to_f64(w.k[0, h])
+        vv = to_f64(w.v[0, h])
+        q = to_f64(w.q[0, h][torch.from_numpy(rows)])
+        t0 = time.perf_counter()
+        O.attention_rows(q, kk, vv, list(range(len(rows))), sets)
+        t_attn += time.perf_counter() - t0
+    scale = Nq / sample_queries
+    return dict(t_index=t_index * scale, t_attn_layer=t_attn * scale, t_attn_sample=t_attn,
+                threads=_oracle_threads(), sample=f"router + indexer scores + top-{topk} and attention of all {H} "
+                f"heads on {sample_queries} random queries of the chunk, scaled to {Nq} queries")
+
+
+def time_steps(fns, steps, warmup, stream):
+    """Run `fns` (list of phases) per step; HIP events bracket every phase on `stream`."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = [float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])) for j in range(len(fns))]
+    total = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]))
+    return total, phases, wall
+
+
+def attn_src_digest():
+    h = hashlib.sha256()
+    for p in ATTN_SRCS:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: the reference run that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps, "attn_src_sha256": attn_src_digest()}),
+          flush=True)
+
+
+def traffic_record():
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if
+    they were taken on the attention source as it is now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("attn_src_sha256") != attn_src_digest():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
 
 
 def main():
@@ -139,49 +243,72 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--n", type=int, default=131072, help="sequence length (the workload is stated at 131072)")
+    ap.add_argument("--workload", default="mixed128k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: the hot path is measured on one device's share; --gpus {args.gpus} is "
-              f"not supported (multi-GPU sharding is a design in DESIGN.md, not built).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the hot path runs on one device's share of heads; --gpus {args.gpus} is "
+              f"not supported (how the path would shard is described in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda", 0)
-    log(f"[bench] generating the mixed-pattern workload N={args.n}")
-    w = synth.mixed_layer(N=args.n)
+    desc, make = WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload}")
+    w = make()
     B, H, Hkv, Nq, Nk, d = w.shape
     q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
-    layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        layer(q, k, v)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        layer.build_indices(q, k)
-        ev[i][1].record(stream)
-        layer.attention(q, k, v)
-        ev[i][2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    ms_index = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
-    ms_attn = float(np.mean([b.elapsed_time(c) for a, b, c in ev]))
+    extra = {}
+
+    if args.workload.startswith("indexer"):
+        qi, ki, wt = w.extra["q_idx"].to(dev), w.extra["k_idx"].to(dev), w.extra["w"].to(dev)
+        topk, route = w.extra["topk"], w.extra["route_heads"]
+        tok = dsa.TokenIndex.empty(1, Nq, topk, dev)
+        shape = dsa.Shape(1, 1, 1, Nq, Nk, 128, Nk - Nq)
+        ws = torch.empty(dsa.workspace_size(dsa.OP_TOKENS, shape, [qi.shape[1], route, topk]), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty(1, H, Nq, d, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(1, H, Nq, dtype=torch.float32, device=dev)
+        aws = torch.empty(dsa.workspace_size(dsa.OP_ATTN, dsa.make_shape(q, k)), dtype=torch.uint8, device=dev)
+        build = lambda: dsa.build_index_tokens(qi, ki, wt, topk, tok, route_heads=route, ws=ws)
+        attn = lambda: dsa.sparse_prefill_attn(q, k, v, [dsa.TOKEN] * H, tok=tok, out_dtype=dsa.OUT_BF16, o=o,
+                                               lse=lse, ws=aws)
+        log(f"[bench] timing {args.steps} steps")
+        ms_step, (ms_index, ms_attn), wall = time_steps([build, attn], args.steps, args.warmup, stream)
+        n_sel = int(tok.count.sum().item()) * H
+        f_sel = 4 * d * n_sel
+        hsel = qi.shape[1] if route == 0 else route
+        pos = np.arange(Nq, dtype=np.float64) + (Nk - Nq)
+        extra["indexer_flop"] = float(2 * 128 * hsel * (pos + 1).sum())
+        extra["indexer_tflops"] = round(extra["indexer_flop"] / (ms_index * 1e-3) / 1e12, 2)
+        extra["gather_bytes"] = n_sel * 2 * d * 2
+        extra["token_attn_gbs"] = round(extra["gather_bytes"] / (ms_attn * 1e-3) / 1e9, 1)
+    else:
+        layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} steps")
+        ms_step, (ms_index, ms_attn), wall = time_steps([lambda: layer.build_indices(q, k),
+                                                         lambda: layer.attention(q, k, v)],
+                                                        args.steps, args.warmup, stream)
+        f_sel = 4 * d * selected_count_layer(layer, w)
+        if args.workload.startswith("thresh"):
+            # the dense causal comparison on the same inputs (informative)
+            dense_o = torch.empty(B, H, Nq, d, dtype=torch.bfloat16, device=dev)
+            dws = torch.empty(dsa.workspace_size(dsa.OP_ATTN, dsa.make_shape(q, k)), dtype=torch.uint8, device=dev)
+            dense = lambda: dsa.sparse_prefill_attn(q, k, v, [dsa.DENSE] * H, out_dtype=dsa.OUT_BF16, o=dense_o,
+                                                    ws=dws, want_lse=False)
+            ms_dense, _, _ = time_steps([dense], 2, 1, stream)
+            diff = (layer.o.float() - dense_o.float()).abs()
+            extra["ms_dense_attn"] = round(ms_dense, 3)
+            extra["speedup_vs_dense"] = round(ms_dense / ms_step, 2)
+            extra["sparse_vs_dense_max_abs"] = round(float(diff.max()), 4)
+            extra["sparse_vs_dense_mean_abs"] = round(float(diff.mean()), 5)
     log(f"[bench] {ms_step:.3f} ms/step (index {ms_index:.3f}, attention {ms_attn:.3f}); wall {wall:.2f}s")
-    f_sel = 4 * d * selected_count(layer, w)
-    dense = 4 * d * H * (Nq * (Nq + 1) // 2)
+    dense_flop = 4 * d * H * (Nq * (Nq + 1) // 2 + Nq * w.q_offset)
     tflops = f_sel / (ms_step * 1e-3) / 1e12
     attn_tflops = f_sel / (ms_attn * 1e-3) / 1e12
     rec = {
@@ -197,26 +324,27 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"mixed-pattern layer, 32 Q / 8 KV heads, d=128, N={Nk}, heads 0-10 A-shape "
-                               f"(sink 128, local 2048), 11-26 Vertical-Slash (last_q 64, 1000 cols, 4096 diags), "
-                               f"27-31 block top-128 of 64",
-                   "batch": B, "seq_len": Nk, "heads": H, "kv_heads": Hkv,
-                   "ms_index": round(ms_index, 4), "ms_attn": round(ms_attn, 4),
-                   "f_sel": f_sel, "density": round(f_sel / dense, 5)},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_kernel (sparse_prefill_attn)"},
+        "config": {"workload": desc, "name": args.workload, "batch": B, "seq_len": Nk, "heads": H, "kv_heads": Hkv,
+                   "ms_index": round(ms_index, 4), "ms_attn": round(ms_attn, 4), "f_sel": f_sel,
+                   "density": round(f_sel / dense_flop, 5), **extra},
     }
+    if args.workload.startswith("indexer"):
+        rec["roofline"] = {"bound": "mfma", "achieved": extra["indexer_tflops"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(extra["indexer_tflops"] / PEAK_BF16_TFLOPS, 4),
+                           "traffic": None, "kernel": "qk_heads_kernel + token_select_kernel (build_index_tokens)"}
+    else:
+        rec["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic_record() if args.workload == "mixed128k" else None,
+                           "kernel": "attn_kernel (sparse_prefill_attn)"}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        cb = cpu_baseline(w, layer)
+        cb = cpu_baseline_indexer(w) if args.workload.startswith("indexer") else cpu_baseline(w)
         t_cpu = cb["t_index"] + cb["t_attn_layer"]
         rec["cpu_baseline"] = {
             "value": round(f_sel / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cb["threads"], "kind": "oracle",
-            "sample": f"fp64 numpy oracle: one Vertical-Slash head and one block head index build (scaled by head "
-                      f"count) + attention on {cb['sample_rows']} random rows per head (scaled to {Nq} rows); "
-                      f"t_index {cb['t_index']:.2f}s, t_attn(sample) {cb['t_attn_sample']:.2f}s, "
-                      f"layer estimate {t_cpu:.1f}s",
+            "sample": f"fp64 numpy oracle, {cb['sample']}; t_index {cb['t_index']:.2f}s, attention sample "
+                      f"{cb['t_attn_sample']:.2f}s, layer estimate {t_cpu:.1f}s ({t_cpu * 1e3:.0f} ms per layer)",
         }
     print(json.dumps(rec), flush=True)
 
