@@ -105,7 +105,7 @@ def _oracle_threads():
     return threads
 
 
-def cpu_baseline(w, sample_rows=192, seed=0):
+def cpu_baseline(w, sample_rows=512, seed=0):
     """The fp64 oracle on a bounded sample of the same workload, scaled to the
     layer.  Every index set is the oracle's own (index rules timed in full for
     every head); attention is timed on `sample_rows` random rows per head and
@@ -225,15 +225,16 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 def traffic_record():
-    """HBM bytes per attention launch from committed rocprofv3 counter runs, if
-    they were taken on the attention source as it is now."""
+    """HBM bytes (read + written) per attention launch, from committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs scaled by the copy calibration, if they were
+    taken on the attention sources as they are now."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("attn_src_sha256") != attn_src_digest():
             return None
-        return rec.get("bytes_per_launch")
+        return rec["bytes_per_launch"]["total"]
     except Exception:
         return None
 

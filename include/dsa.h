@@ -140,7 +140,8 @@ dsa_status build_index_ashape(const dsa_shape* shape, const int32_t* heads, int3
  *   cols = top-nv of v over [0, Nk), diags = top-ns of s over [0, Nk).
  * q, k: device bf16 Q and K.  1 <= last_q <= min(64, Nq); 0 <= nv <= cols_cap,
  * 0 <= ns <= diags_cap, nv, ns <= Nk.  v_scores / s_scores (nullable, device
- * float [B, H, Nk]) receive v and s of the listed heads.  Workspace:
+ * float [B, n_heads, Nk]) receive v and s, row b * n_heads + t holding listed
+ * head heads[t] of batch b (listed order, not head number).  Workspace:
  * dsa_workspace_size(DSA_OP_VS, {n_heads, last_q}). */
 dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k,
                           const int32_t* heads, int32_t n_heads, int32_t last_q,
@@ -157,9 +158,11 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k,
  *   mode DSA_SELECT_THRESHOLD: J with S[I, J] >= max_J' S[I, J'] + log_alpha;
  *   then the union with block 0 (force_first) and block I (force_diag).
  * block in {64, 128}; q_offset must be 0; out.cap >= the largest count (top-k:
- * min(nqb, topk + forced); threshold: nqb).  qbar ([B, H, nqb, d] bf16), kbar
- * ([B, Hkv, nkb, d] bf16) and scores ([B, H, nqb, nkb] float, -inf above the
- * diagonal) are nullable outputs for inspection.  Workspace:
+ * min(nqb, topk + forced); threshold: nqb).  Nullable outputs for inspection:
+ * qbar ([B, H, nqb, d] bf16, indexed by head number, rows of listed heads
+ * written), kbar ([B, Hkv, nkb, d] bf16, rows of the listed heads' KV heads
+ * written) and scores ([B, n_heads, nqb, nkb] float in listed order, -inf for
+ * J > I).  Workspace:
  * dsa_workspace_size(DSA_OP_BLOCK, {n_heads, block}). */
 dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* k,
                              const int32_t* heads, int32_t n_heads, int32_t block,
