@@ -35,6 +35,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 namespace dsa {
@@ -288,6 +289,18 @@ __device__ __forceinline__ uint32_t causal_mask32(int top) {   // bits c <= top
 #ifndef DSA_ATTN_WAVES_PER_SIMD
 #define DSA_ATTN_WAVES_PER_SIMD 2
 #endif
+// Wave priority around MFMA groups (s_setprio): a wave that reaches its MFMAs
+// issues them ahead of the other waves' softmax work on the same SIMD.
+#ifndef DSA_ATTN_SETPRIO
+#define DSA_ATTN_SETPRIO 1
+#endif
+#if DSA_ATTN_SETPRIO
+#define DSA_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define DSA_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define DSA_PRIO_HI() ((void)0)
+#define DSA_PRIO_LO() ((void)0)
+#endif
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_SIMD))) void attn_kernel(
     const AttnArgs a, const Sched sc) {
@@ -443,8 +456,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             mv0 = vbits[2 * cur.kt]; mv1 = vbits[2 * cur.kt + 1];
           }
         }
-        for (int n = 0; have; ++n) {
-          const int stage = n & 1;
+        // One tile step on ring stage `stage` (a compile-time constant, so every
+        // LDS address below is a lane-constant register plus an immediate).
+        auto step = [&](auto stage_c) {
+          constexpr int stage = decltype(stage_c)::value;
           wait_vm();
           __syncthreads();                       // tile n landed; every wave is done with tile n - 1
           Entry nxt;
@@ -498,18 +513,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const uint32_t part = kb == 0 ? (uint32_t)(swin >> 32) : (uint32_t)swin;
               M = (__builtin_bitreverse32(part) | (kb == 0 ? mv0 : mv1)) & causal_mask32(ktop);
             } else if (mode == M_GATHER) {
+              // staged columns ascend: the keys <= iq are a prefix of the chunk
               const int base = cur.kt * TK + 32 * kb;
               const int cnt = max(0, min(32, cur.cnt - 32 * kb));
-              int lo = 0, hi = cnt;
-              while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (s_cols[base + mid] <= iq) lo = mid + 1; else hi = mid;
+              if (cnt == 32 && s_cols[base + 31] <= iq) {
+                M = ~0u;
+              } else {
+                int lo = 0, hi = cnt;
+                while (lo < hi) {
+                  const int mid = (lo + hi) >> 1;
+                  if (s_cols[base + mid] <= iq) lo = mid + 1; else hi = mid;
+                }
+                M = lo >= 32 ? ~0u : ((1u << lo) - 1u);
               }
-              M = lo >= 32 ? ~0u : ((1u << lo) - 1u);
             }
             if (!row_ok) M = 0u;
-            const bool masked = mode != M_NONE;
             if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) continue;
+            const bool masked = __builtin_amdgcn_ballot_w64(M != ~0u) != 0;
 
             // ---- S^T = K Q^T for these 32 keys (eight K fragments read first)
             f32x16 sacc;
@@ -519,27 +539,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             u32x4 kf[8];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(sk + row * 256 + swz_k(row, 2 * ks + hh) * 16);
+            DSA_PRIO_HI();
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
               sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sacc, 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            DSA_PRIO_LO();
 
-            // ---- mask, online softmax (raw scores; the scale is folded into exp2)
-            const uint32_t mk = M >> (4 * hh);
-            float mx = -INFINITY;
+            // ---- mask (one wave-uniform branch), online softmax on raw scores
+            // (the scale is folded into exp2)
+            if (masked) {
+              const uint32_t mk = M >> (4 * hh);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float x = sacc[v];
-              if (masked) {
+              for (int v = 0; v < 16; ++v) {
                 const int pos = 8 * (v >> 2) + (v & 3);
                 const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
-                x = __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
+                sacc[v] = __uint_as_float((__float_as_uint(sacc[v]) & keep) | (0xff800000u & ~keep));
               }
-              sacc[v] = x;
-              mx = fmaxf(mx, x);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+            float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+            for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sacc[v]), sacc[v + 1]);
+            mx = fmaxf(mx, sacc[15]);
+            {
+              // rows live in lanes l and l ^ 32: swap halves and take the max
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+              mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+            }
             const bool grow = mx > m_run + 8.0f;
             if (__builtin_amdgcn_ballot_w64(grow) != 0) {
               const float mnew = grow ? mx : m_run;
@@ -580,6 +607,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
                 yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_short4_t*)(sv + rowb * 256 + swz_v(rowb, cch) * 16 + v_half));
               }
+              DSA_PRIO_HI();
 #pragma unroll
               for (int db = 0; db < 4; ++db) {
                 const short8_t ab = {ya[db][0], ya[db][1], ya[db][2], ya[db][3], yb[db][0], yb[db][1], yb[db][2], yb[db][3]};
@@ -587,11 +615,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               }
               __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
               __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+              DSA_PRIO_LO();
             }
           }
           cur = nxt;
           have = have_n;
           ms0 = ns0; ms1 = ns1; ms2 = ns2; mv0 = nv0; mv1 = nv1;
+        };
+        while (have) {
+          step(std::integral_constant<int, 0>{});
+          if (!have) break;
+          step(std::integral_constant<int, 1>{});
         }
         if (!(it.kind == 1 && gcursor < gcount)) break;
         __syncthreads();                         // the last tile's gathered columns are no longer read
