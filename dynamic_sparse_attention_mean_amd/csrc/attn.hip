@@ -162,9 +162,16 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 // 16 bytes per lane straight from global memory into LDS; lane l of the wave
-// lands at lds_base + 16 l (lds_base is wave-uniform).
-__device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+// lands at LDS byte address lds_addr + 16 l (lds_addr is wave-uniform).
+// Issued from inline assembly on purpose: the compiler does not track these
+// LDS writes, so it adds no wait of its own before the LDS reads of the other
+// ring stage (its own wait would drain the DMA just issued for the next tile).
+// The explicit vmcnt wait at the top of each step orders a tile's DMA before
+// the reads of its stage; the "memory" clobber keeps the compiler from moving
+// LDS accesses across the issue.  The instruction has no register results.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_addr) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -174,18 +181,30 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
 
+// Wave-uniform read of data the kernel never writes, through the constant
+// address space so that it becomes a scalar load (lgkmcnt, not vmcnt): the
+// K/V DMAs are then the only vector memory operations in the tile loop, and
+// the vmcnt wait at the top of a step waits for nothing else.
+typedef const __attribute__((address_space(4))) int32_t c_i32_t;
+typedef const __attribute__((address_space(4))) uint32_t c_u32_t;
+__device__ __forceinline__ int ldc(const int32_t* p, size_t i) { return ((c_i32_t*)p)[i]; }
+__device__ __forceinline__ uint32_t ldc(const uint32_t* p, size_t i) { return ((c_u32_t*)p)[i]; }
+__device__ __forceinline__ bool test_bit_c(const uint32_t* bm, int i) { return (ldc(bm, i >> 5) >> (i & 31)) & 1u; }
+
 // One entry of a pair's tile stream.
 struct Entry {
   int kind;    // 0 key tile, 1 gather chunk, -1 none
   int kt;      // key tile index, or gather chunk index
   int cnt;     // valid keys of a gather chunk
   int flags;   // bit h: query tile h of the pair uses this entry
+  int full;    // VS strip tile: bit h set if every entry is selected for query tile h
 };
 
 struct Item {
   int bh, kvh, kind, P0, last_pos, tq1;
   // VS
   const int32_t* a2;       // strip tile offsets (relative to tq1), ascending
+  const uint32_t* fb;      // "full" bits of tile offsets
   int nstrip;
   // BLOCK
   const int32_t* l0;       // list of query block I0 (or of the shared block)
@@ -204,15 +223,15 @@ struct Cursor {
   int x0n, x1n;            // prefetched successors of the heads
 };
 
-__device__ __forceinline__ int list_at(const int32_t* L, int n, int i) { return i < n ? L[i] : 0x7fffffff; }
+__device__ __forceinline__ int list_at(const int32_t* L, int n, int i) { return i < n ? ldc(L, i) : 0x7fffffff; }
 
 __device__ __forceinline__ void cursor_init(const Item& it, Cursor& c) {
   c.n = 0;
   c.raw = 0;
   c.i0 = c.i1 = 0;
   c.x0 = c.x1 = c.x0n = c.x1n = 0x7fffffff;
-  if (it.kind == 1) c.raw = it.nstrip > 0 ? it.a2[0] : 0;
-  else if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? it.l0[0] : 0;
+  if (it.kind == 1) c.raw = it.nstrip > 0 ? ldc(it.a2, 0) : 0;
+  else if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? ldc(it.l0, 0) : 0;
   else if (it.kind == 2) {
     c.x0 = list_at(it.l0, it.n0, 0); c.x1 = list_at(it.l1, it.n1, 0);
     c.x0n = list_at(it.l0, it.n0, 1); c.x1n = list_at(it.l1, it.n1, 1);
@@ -230,11 +249,16 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   e.cnt = 0;
   e.flags = 3;
   e.kind = 0;
+  e.full = 0;
   const int n = c.n++;
   if (it.kind == 1) {
     if (n < it.nstrip) {
-      e.kt = it.tq1 - c.raw;
-      c.raw = (n + 1 < it.nstrip) ? it.a2[n + 1] : 0;
+      // tile offset of query tile h of the pair is raw - 1 + h; offsets >= 1 may be full
+      const int r = c.raw;
+      e.kt = it.tq1 - r;
+      if (r >= 2 && test_bit_c(it.fb, r - 1)) e.full |= 1;
+      if (r >= 1 && test_bit_c(it.fb, r)) e.full |= 2;
+      c.raw = (n + 1 < it.nstrip) ? ldc(it.a2, n + 1) : 0;
     } else {
       e.kind = 1;
       e.kt = n - it.nstrip;
@@ -242,7 +266,7 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
     }
   } else if (it.kind == 2 && it.per == 2) {
     e.kt = c.raw * 2 + (n & 1);
-    if (n & 1) c.raw = ((n >> 1) + 1 < it.n0) ? it.l0[(n >> 1) + 1] : 0;
+    if (n & 1) c.raw = ((n >> 1) + 1 < it.n0) ? ldc(it.l0, (n >> 1) + 1) : 0;
   } else if (it.kind == 2) {
     const int x = min(c.x0, c.x1);
     e.kt = x;
@@ -263,12 +287,12 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
 // gather chunk computes each row's key.
 template <bool IS_V>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ base, int Nk, const Entry& e,
-                                           const int32_t* s_cols, char* lds, int w, int lane, uint32_t off) {
+                                           const int32_t* s_cols, uint32_t lds, int w, int lane, uint32_t off) {
   if (e.flags == 0) return;
   if (e.kind == 0 && e.kt * TK + TK <= Nk) {
     const char* tb = (const char*)(base + (size_t)e.kt * TK * 128);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(tb + off + 4096 * j, (lds_void_t*)(lds + (4 * j + w) * 1024));
+    for (int j = 0; j < 4; ++j) dma16(tb + off + 4096 * j, lds + (4 * j + w) * 1024);
     return;
   }
 #pragma unroll
@@ -278,7 +302,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ base, in
     int key;
     if (e.kind == 1) key = s_cols[e.kt * TK + (r < e.cnt ? r : 0)];
     else key = min(e.kt * TK + r, Nk - 1);
-    dma16(base + (size_t)key * 128 + c * 8, (lds_void_t*)(lds + (4 * j + w) * 1024));
+    dma16(base + (size_t)key * 128 + c * 8, lds + (4 * j + w) * 1024);
   }
 }
 
@@ -325,6 +349,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
   const int G = l >> 4, si = l & 15;
   const int v_row0 = 4 * (G >> 1) + (si >> 2);           // + 32 kb + 16 s2 (+ 8)
   const int v_half = (si & 1) * 8;
+  // LDS byte address of the ring; stage s, K (0) or V (1) at + (2 s + kv) * 16 KB
+  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)&s_kv[0][0][0]);
 
   for (int qi = 0; qi < sc.nq; ++qi) {
     const int g = (myq + qi) % sc.nq;
@@ -353,6 +379,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       it.per = 1;
       it.n0 = it.n1 = 0;
       it.a2 = nullptr;
+      it.fb = nullptr;
       it.l0 = it.l1 = nullptr;
 
       const uint16_t* kbp = a.k + ((size_t)(b * a.Hkv + it.kvh) * a.Nk) * 128;
@@ -361,7 +388,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
 
       const int qrow = r0 + TQ * ih + 32 * wr + qn;
       const int P0w = it.P0 + TQ * ih;                // first position of this wave's query tile
-      const int iq = P0w + 32 * wr + qn;               // absolute position of this lane's row
+      const int R0w = P0w + 32 * wr;                   // position of this wave's first row
+      const int iq = R0w + qn;                         // absolute position of this lane's row
       const bool row_ok = qrow < a.Nq;
       bf16x8 qf[8];
 #pragma unroll
@@ -370,6 +398,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         if (row_ok) x = *(const u32x4*)(qbp + (size_t)qrow * 128 + 16 * ks + 8 * hh);
         qf[ks] = __builtin_bit_cast(bf16x8, x);
       }
+      // Take the Q fragments in before the tile loop: otherwise the compiler
+      // waits for these loads at their first use inside the loop, where the
+      // wait would also drain the K/V DMA in flight.
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) asm volatile("" :: "v"(qf[ks]));
       f32x16 acc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -377,26 +410,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
-      const uint32_t* fbits = nullptr;
       const uint32_t* sbits = nullptr;
       const uint32_t* vbits = nullptr;
       int gcursor = 0, gcount = 0;
       if (it.kind == 1) {
         it.a2 = a.a2list + (size_t)it.bh * a.acap;
-        fbits = a.fbits + (size_t)it.bh * a.aw;
+        it.fb = a.fbits + (size_t)it.bh * a.aw;
         sbits = a.sbits + (size_t)it.bh * a.sw;
         vbits = a.vbits + (size_t)it.bh * a.vw;
-        it.nstrip = a.a2le[(size_t)it.bh * a.acap + it.tq1];
-        gcount = min(a.cols_count[it.bh], a.cols_cap);
+        it.nstrip = ldc(a.a2le, (size_t)it.bh * a.acap + it.tq1);
+        gcount = min(ldc(a.cols_count, it.bh), a.cols_cap);
       } else if (it.kind == 2) {
         it.per = a.block / TK;
         const int I0 = it.P0 / a.block;
         it.l0 = a.bidx + ((size_t)it.bh * a.nqb + I0) * a.bcap;
-        it.n0 = min(a.bcount[(size_t)it.bh * a.nqb + I0], a.bcap);
+        it.n0 = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I0), a.bcap);
         it.l1 = it.l0;
         if (it.per == 1 && I0 + 1 < a.nqb && r0 + TQ < a.Nq) {
           it.l1 = a.bidx + ((size_t)it.bh * a.nqb + I0 + 1) * a.bcap;
-          it.n1 = min(a.bcount[(size_t)it.bh * a.nqb + I0 + 1], a.bcap);
+          it.n1 = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I0 + 1), a.bcap);
         }
       }
 
@@ -443,60 +475,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         Entry cur;
         cur.kind = -1;
         cur.flags = 0;
-        uint32_t ms0 = 0u, ms1 = 0u, ms2 = 0u, mv0 = 0u, mv1 = 0u;
+        cur.full = 0;
         bool have = cursor_has_next(it, cc);
         if (have) {
           cur = cursor_next(it, cc);
-          issue_tile<false>(kbp, a.Nk, cur, s_cols, s_kv[0][0], w, l, off_k);
-          issue_tile<true>(vbp, a.Nk, cur, s_cols, s_kv[0][1], w, l, off_v);
-          if (it.kind == 1 && cur.kind == 0) {
-            // offsets iq - key for the 64 keys of the tile: window [top - 63, top]
-            const int wi = row_ok ? max(((iq - cur.kt * TK - 63) >> 5) + 2, 0) : 0;
-            ms0 = sbits[wi]; ms1 = sbits[wi + 1]; ms2 = sbits[wi + 2];
-            mv0 = vbits[2 * cur.kt]; mv1 = vbits[2 * cur.kt + 1];
-          }
+          issue_tile<false>(kbp, a.Nk, cur, s_cols, ring, w, l, off_k);
+          issue_tile<true>(vbp, a.Nk, cur, s_cols, ring + TK * 256, w, l, off_v);
         }
         // One tile step on ring stage `stage` (a compile-time constant, so every
         // LDS address below is a lane-constant register plus an immediate).
         auto step = [&](auto stage_c) {
           constexpr int stage = decltype(stage_c)::value;
+          // ---- this wave's view of the entry (key tiles wholly after its rows,
+          // and waves with no row inside the chunk, skip)
+          int mode;
+          if (!((cur.flags >> ih) & 1) || (cur.kind == 0 && cur.kt * TK > P0w + TQ - 1) || R0w > it.last_pos)
+            mode = M_SKIP;
+          else if (cur.kind == 1) mode = M_GATHER;
+          else if (it.kind == 1) mode = ((cur.full >> ih) & 1) ? M_NONE : M_VS;
+          else mode = (cur.kt * TK + TK - 1 > P0w) ? M_CAUSAL : M_NONE;
+          // diagonal-bitmap words covering this wave's windows and the tile's
+          // column bits (scalar loads, issued before the wait)
+          uint32_t W0 = 0u, W1 = 0u, W2 = 0u, W3 = 0u, mv0 = 0u, mv1 = 0u;
+          int wbase = 0;
+          if (mode == M_VS) {
+            wbase = R0w - cur.kt * TK - 63;               // window start of this wave's row 0 (>= -63)
+            const uint32_t* swp = sbits + ((wbase >> 5) + 2);
+            W0 = ldc(swp, 0); W1 = ldc(swp, 1); W2 = ldc(swp, 2); W3 = ldc(swp, 3);
+            mv0 = ldc(vbits, 2 * cur.kt); mv1 = ldc(vbits, 2 * cur.kt + 1);
+          }
           wait_vm();
           __syncthreads();                       // tile n landed; every wave is done with tile n - 1
           Entry nxt;
           nxt.kind = -1;
           nxt.flags = 0;
-          uint32_t ns0 = 0u, ns1 = 0u, ns2 = 0u, nv0 = 0u, nv1 = 0u;
+          nxt.full = 0;
           const bool have_n = cursor_has_next(it, cc);
           if (have_n) {
             nxt = cursor_next(it, cc);
-            issue_tile<false>(kbp, a.Nk, nxt, s_cols, s_kv[stage ^ 1][0], w, l, off_k);
-            issue_tile<true>(vbp, a.Nk, nxt, s_cols, s_kv[stage ^ 1][1], w, l, off_v);
-            if (it.kind == 1 && nxt.kind == 0) {
-              const int wi = row_ok ? max(((iq - nxt.kt * TK - 63) >> 5) + 2, 0) : 0;
-              ns0 = sbits[wi]; ns1 = sbits[wi + 1]; ns2 = sbits[wi + 2];
-              nv0 = vbits[2 * nxt.kt]; nv1 = vbits[2 * nxt.kt + 1];
-            }
+            issue_tile<false>(kbp, a.Nk, nxt, s_cols, ring + (stage ^ 1) * 2 * TK * 256, w, l, off_k);
+            issue_tile<true>(vbp, a.Nk, nxt, s_cols, ring + ((stage ^ 1) * 2 + 1) * TK * 256, w, l, off_v);
           }
           const char* sk = s_kv[stage][0];
           const lds_char_t* sv = (const lds_char_t*)s_kv[stage][1];
 
-          // ---- this wave's view of the entry
-          int mode;
-          if (!((cur.flags >> ih) & 1)) mode = M_SKIP;
-          else if (cur.kind == 1) mode = M_GATHER;
-          else if (it.kind == 1) {
-            const int aw_ = P0w / TK - cur.kt;
-            mode = (aw_ >= 1 && test_bit(fbits, aw_)) ? M_NONE : M_VS;
-          } else {
-            mode = (cur.kt * TK + TK - 1 > P0w) ? M_CAUSAL : M_NONE;
-          }
           // 64-bit window of diagonal bits for this lane's row (bit b <-> offset lo + b)
           uint64_t swin = 0;
           if (mode == M_VS) {
-            const int lo = iq - cur.kt * TK - 63;
-            const int sh = lo & 31;
-            const uint64_t lo64 = ((uint64_t)ms1 << 32) | ms0;
-            swin = sh ? ((lo64 >> sh) | ((uint64_t)ms2 << (64 - sh))) : lo64;
+            const int sh = (wbase & 31) + qn;            // 0 .. 62
+            const uint64_t lo64 = ((uint64_t)W1 << 32) | W0;
+            const uint64_t hi64 = ((uint64_t)W3 << 32) | W2;
+            swin = sh ? ((lo64 >> sh) | (hi64 << (64 - sh))) : lo64;
           }
 
 #pragma unroll
@@ -620,7 +649,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
           cur = nxt;
           have = have_n;
-          ms0 = ns0; ms1 = ns1; ms2 = ns2; mv0 = nv0; mv1 = nv1;
         };
         while (have) {
           step(std::integral_constant<int, 0>{});
