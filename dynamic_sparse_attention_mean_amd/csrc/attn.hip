@@ -773,8 +773,12 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  // Queue assignment: estimate each head's cost (key tiles over all its query
-  // tiles), longest first into the least-loaded queue.
+  // Queue assignment.  Each head's cost is estimated (key tiles over all its
+  // query tiles); the Q heads that share a KV head go to the same queue, so
+  // that the items running together on one XCD stream the same K/V tiles
+  // through that XCD's L2.  Groups are placed longest first into the
+  // least-loaded queue; within a queue, consecutive items are the group's
+  // heads at the same query rows.
   struct HC { double cost; int bh; };
   std::vector<HC> heads;
   for (int b = 0; b < a.B; ++b)
@@ -789,17 +793,26 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
     }
   if ((e = launch_token_attention(a, st)) != hipSuccess) return e;
   if (heads.empty()) return hipSuccess;
-  std::stable_sort(heads.begin(), heads.end(), [](const HC& x, const HC& y) { return x.cost > y.cost; });
+  const int rep = a.H / a.Hkv;
+  struct GC { double cost; int key; std::vector<int> bh; };
+  std::vector<GC> groups;
+  for (const HC& x : heads) {
+    const int key = (x.bh / a.H) * a.Hkv + (x.bh % a.H) / rep;   // b * Hkv + kv head
+    if (groups.empty() || groups.back().key != key) groups.push_back({0.0, key, {}});
+    groups.back().cost += x.cost;
+    groups.back().bh.push_back(x.bh);
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const GC& x, const GC& y) { return x.cost > y.cost; });
   Sched sc;
   sc.T2 = T2;
-  sc.nq = std::min<int>(kMaxQueues, (int)heads.size());
+  sc.nq = std::min<int>(kMaxQueues, (int)groups.size());
   std::vector<std::vector<int>> qh(sc.nq);
   std::vector<double> load(sc.nq, 0.0);
-  for (const HC& x : heads) {
+  for (const GC& x : groups) {
     int best = 0;
     for (int g = 1; g < sc.nq; ++g) if (load[g] < load[best]) best = g;
     load[best] += x.cost;
-    qh[best].push_back(x.bh);
+    for (int bh : x.bh) qh[best].push_back(bh);
   }
   int pos = 0;
   for (int g = 0; g < sc.nq; ++g) {
