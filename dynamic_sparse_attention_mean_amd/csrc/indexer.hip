@@ -250,15 +250,31 @@ __global__ __launch_bounds__(1024) void token_select_kernel(const float* scores,
 // ---------------------------------------------------------------- token attention
 constexpr int TA_THREADS = 256;
 constexpr int TA_MAXTOK = 4096;
+constexpr int TA_U = 8;            // token rows each 16-lane group keeps in flight
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the total.
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror joins the
+// two quads of each 8-lane half, row_mirror joins the two halves.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
 
 // One workgroup per (head, query); heads outermost so a head's K/V stay cached.
+// A 16-lane group owns one token row at a time (lane = 8 dims, 16 bytes of the
+// row), the four groups of a wave take four tokens, and every group keeps
+// TA_U rows in flight: the gathered K rows (scores) and V rows (output) stream
+// with enough loads outstanding to cover the cache latency.
 __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                                 int H, int Hkv, int Nq, int Nk, const int32_t* tidx,
                                                                 const int32_t* tcount, int tcap, void* o, float* lse,
                                                                 int out_f32, int B, HeadList th) {
   __shared__ float s_p[TA_MAXTOK];
   __shared__ int32_t s_t[TA_MAXTOK];
-  __shared__ float s_red[4][128];
+  __shared__ float s_red[4][4][128];
   __shared__ float s_ms[8];
   const int bid = blockIdx.x;
   const int h = th.h[bid / (Nq * B)];
@@ -266,6 +282,7 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
   const int b = rem / Nq, i = rem % Nq;
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int sub = l & 15, tg = l >> 4;
   const int n = min(min(tcount[(size_t)b * Nq + i], tcap), TA_MAXTOK);
   const int32_t* tl = tidx + ((size_t)b * Nq + i) * tcap;
   for (int x = tid; x < n; x += TA_THREADS) {
@@ -276,33 +293,40 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
   const uint16_t* qrow = q + (((size_t)b * H + h) * Nq + i) * 128;
   const uint16_t* kb = k + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
   const uint16_t* vb = v + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
-  // scores: 16 lanes per token (8 dims each), 4 tokens per wave step
-  const int sub = l & 15, tg = l >> 4;
   const u32x4 qx = *(const u32x4*)(qrow + sub * 8);
+  // scores in log2 units: q . k * log2(e) / sqrt(128)
+  const float scale2 = 1.4426950408889634f * 0.08838834764831845f;
   float qv[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { qv[2 * e] = bf16_lo(qx[e]); qv[2 * e + 1] = bf16_hi(qx[e]); }
-  const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
+  for (int e = 0; e < 4; ++e) { qv[2 * e] = bf16_lo(qx[e]) * scale2; qv[2 * e + 1] = bf16_hi(qx[e]) * scale2; }
+
+  // ---- scores: token x = x0 + 16 u + 4 wv + tg
   float mloc = -INFINITY;
-  for (int x0 = wv * 4; x0 < n; x0 += 16) {
-    const int x = x0 + tg;
-    float d = 0.f;
-    int j = -1;
-    if (x < n) j = s_t[x];
-    if (j >= 0) {
-      const u32x4 kx = *(const u32x4*)(kb + (size_t)j * 128 + sub * 8);
+  for (int x0 = 0; x0 < n; x0 += 16 * TA_U) {
+    u32x4 kx[TA_U];
+    int jj[TA_U];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        d = __builtin_fmaf(qv[2 * e], bf16_lo(kx[e]), d);
-        d = __builtin_fmaf(qv[2 * e + 1], bf16_hi(kx[e]), d);
-      }
+    for (int u = 0; u < TA_U; ++u) {
+      const int x = x0 + 16 * u + 4 * wv + tg;
+      jj[u] = x < n ? s_t[x] : -1;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      kx[u] = jj[u] >= 0 ? *(const u32x4*)(kb + (size_t)jj[u] * 128 + sub * 8) : z;
     }
 #pragma unroll
-    for (int o2 = 8; o2 >= 1; o2 >>= 1) d += __shfl_xor(d, o2, 64);
-    if (x < n && sub == 0) {
-      const float s = j >= 0 ? d * scale : -INFINITY;
-      s_p[x] = s;
-      mloc = fmaxf(mloc, s);
+    for (int u = 0; u < TA_U; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = __builtin_fmaf(qv[2 * e], bf16_lo(kx[u][e]), d);
+        d = __builtin_fmaf(qv[2 * e + 1], bf16_hi(kx[u][e]), d);
+      }
+      d = row16_sum(d);
+      const int x = x0 + 16 * u + 4 * wv + tg;
+      const float sc = jj[u] >= 0 ? d : -INFINITY;
+      if (x < n) {
+        if (sub == 0) s_p[x] = sc;
+        mloc = fmaxf(mloc, sc);
+      }
     }
   }
   mloc = wave_max(mloc);
@@ -311,34 +335,53 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
   const float m = fmaxf(fmaxf(s_ms[0], s_ms[1]), fmaxf(s_ms[2], s_ms[3]));
   float lsum = 0.f;
   for (int x = tid; x < n; x += TA_THREADS) {
-    const float p = (m == -INFINITY) ? 0.f : __expf(s_p[x] - m);
+    const float p = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_p[x] - m);
     s_p[x] = p;
     lsum += p;
   }
   lsum = wave_sum(lsum);
-  __syncthreads();
   if (l == 0) s_ms[4 + wv] = lsum;
-  // O: lane l owns dims 2l, 2l+1; wave wv walks tokens wv, wv+4, ...
-  float o0 = 0.f, o1 = 0.f;
-  for (int x = wv; x < n; x += 4) {
-    const int j = s_t[x];
-    if (j < 0) continue;
-    const float p = s_p[x];
-    const uint32_t vx = *(const uint32_t*)(vb + (size_t)j * 128 + 2 * l);
-    o0 = __builtin_fmaf(p, bf16_lo(vx), o0);
-    o1 = __builtin_fmaf(p, bf16_hi(vx), o1);
+  __syncthreads();
+
+  // ---- output: lane accumulates dims 8 sub .. +7 over its group's tokens
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int x0 = 0; x0 < n; x0 += 16 * TA_U) {
+    u32x4 vx[TA_U];
+    float pp[TA_U];
+#pragma unroll
+    for (int u = 0; u < TA_U; ++u) {
+      const int x = x0 + 16 * u + 4 * wv + tg;
+      const int j = x < n ? s_t[x] : -1;
+      pp[u] = j >= 0 ? s_p[x] : 0.f;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      vx[u] = j >= 0 ? *(const u32x4*)(vb + (size_t)j * 128 + sub * 8) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < TA_U; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = __builtin_fmaf(pp[u], bf16_lo(vx[u][e]), acc[2 * e]);
+        acc[2 * e + 1] = __builtin_fmaf(pp[u], bf16_hi(vx[u][e]), acc[2 * e + 1]);
+      }
   }
-  s_red[wv][2 * l] = o0;
-  s_red[wv][2 * l + 1] = o1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_red[wv][tg][sub * 8 + e] = acc[e];
   __syncthreads();
   if (tid < 128) {
     const float ltot = s_ms[4] + s_ms[5] + s_ms[6] + s_ms[7];
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    const float val = (s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]) * inv;
+    float sum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+      for (int g2 = 0; g2 < 4; ++g2) sum += s_red[w2][g2][tid];
+    const float val = sum * inv;
     const size_t oi = (((size_t)b * H + h) * Nq + i) * 128 + tid;
     if (out_f32) ((float*)o)[oi] = val;
     else ((uint16_t*)o)[oi] = (uint16_t)f32_to_bf16_bits(val);
-    if (tid == 0 && lse) lse[((size_t)b * H + h) * Nq + i] = ltot > 0.f ? m + __logf(ltot) : -INFINITY;
+    if (tid == 0 && lse) lse[((size_t)b * H + h) * Nq + i] = ltot > 0.f ? (m + __log2f(ltot)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
