@@ -265,6 +265,8 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 0 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
   if (route_heads > 8) return fail(DSA_ERR_UNSUPPORTED, "route_heads > 8");
+  // score rows are written through 32-bit buffer offsets (four rows per wave)
+  if (shape->kv_len > (1 << 27)) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes kv_len <= 2^27");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
   if (!out.idx || !out.count) return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
   if (out.cap < std::min(topk, shape->kv_len)) return fail(DSA_ERR_INVALID_ARG, "out.cap < topk");

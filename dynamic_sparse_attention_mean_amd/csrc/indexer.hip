@@ -138,12 +138,40 @@ __global__ __launch_bounds__(NTI) void qk_heads_kernel(const QkArgs a) {
       dma16(a.keys + (size_t)key * 128 + c * 8, (lds_void_t*)(s_k[stage] + blk * 1024));
     }
   };
+  // Score rows leave one tile late: the stores of tile t are issued right after
+  // the DMA of tile t + 2, so the wait at the top of a tile (vmcnt(0); loads
+  // and stores may complete out of order, so no partial count is safe) finds
+  // both already given a whole tile of compute to finish.  Buffer stores: lanes
+  // with nothing to write get an offset past the end, which the hardware drops.
+  const int nrow = MODE == MODE_ROUTER ? 0 : max(0, min(QPW, a.Nq - q0));
+  const __amdgpu_buffer_rsrc_t orow =
+      __builtin_amdgcn_make_buffer_rsrc(a.out + (size_t)min(q0, a.Nq) * a.Nk, (short)0, nrow * a.Nk * 4, 0x00020000);
+  float pend_v[2][QPW];
+  uint32_t pend_o[2][QPW];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) { pend_v[kb][j] = 0.f; pend_o[kb][j] = 0xFFFFFFFFu; }
+  auto flush = [&]() {
+    if (MODE == MODE_ROUTER) return;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < QPW; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v[kb][j]), orow, pend_o[kb][j], 0, 0);
+  };
   if (ntiles > 0) issue(0, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int stage = t & 1;
-    wait_vm();
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // tile t landed (each wave waited for its own DMA) and every wave is done
+    // reading the stage the next DMA overwrites.  A bare s_barrier: nothing in
+    // global memory needs ordering here.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (t + 1 < ntiles) issue(t + 1, stage ^ 1);
+    if (t > 0) flush();                                // scores of tile t - 1
     const char* sk = s_k[stage];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -185,12 +213,14 @@ __global__ __launch_bounds__(NTI) void qk_heads_kernel(const QkArgs a) {
         for (int j = 0; j < QPW; ++j) {
           const float tot = s[j] + __shfl_xor(s[j], 32, 64);
           const int qq = q0 + j;
-          if (hh == (j & 1) && qq < a.Nq && key <= qq + a.q_offset && key < a.Nk)
-            a.out[(size_t)qq * a.Nk + key] = tot;
+          const bool wr = hh == (j & 1) && qq < a.Nq && key <= qq + a.q_offset && key < a.Nk;
+          pend_v[kb][j] = tot;
+          pend_o[kb][j] = wr ? (uint32_t)(j * a.Nk + key) * 4u : 0xFFFFFFFFu;
         }
       }
     }
   }
+  if (ntiles > 0) flush();                             // scores of the last tile
   if (MODE == MODE_ROUTER) {
     // max over the lanes of each head (the 32 key columns), then r = w * max(0, .)
 #pragma unroll
