@@ -86,3 +86,33 @@ def test_indexer_pipeline_end_to_end():
     for h in range(H):
         ref_o, ref_l = O.attention_rows(f64(w.q[0, h]), f64(w.k[0, h]), f64(w.v[0, h]), list(range(Nq)), sets)
         assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l, f"pipeline head {h}")
+
+
+@pytest.mark.parametrize("N,Nq,topk,kind", [(12000, 6, 500, "binary"), (12000, 4, 700, "zero"),
+                                            (9000, 5, 2048, "binary")])
+def test_token_select_exact_ties(N, Nq, topk, kind):
+    """Integer-valued scores (one indexer head, w = 1, inputs in {0, 1}) are exact
+    in fp32 on both sides, so the GPU's token sets must equal the oracle's top-k
+    exactly, ties to the lower index included.  "zero" makes every score equal:
+    the answer is the first `topk` keys, and the GPU selection takes its
+    fallback path (one bin holds more candidates than it keeps on chip)."""
+    g = torch.Generator().manual_seed(N + topk)
+    if kind == "zero":
+        qi = torch.zeros(Nq, 1, 128)
+    else:
+        qi = (torch.rand(Nq, 1, 128, generator=g) < 0.5).float()
+    ki = (torch.rand(N, 128, generator=g) < 0.5).float()
+    wt = torch.ones(Nq, 1)
+    qi, ki = qi.to(torch.bfloat16), ki.to(torch.bfloat16)
+    out = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+    dsa.build_index_tokens(qi.to(DEV), ki.to(DEV), wt.to(DEV), topk, out)
+    torch.cuda.synchronize()
+    qo = N - Nq
+    qf, kf = f64(qi), f64(ki)
+    for i in range(Nq):
+        p = i + qo
+        sc = O.indexer_row(qf[i], kf, wt[i].double().numpy(), p)
+        want = O.token_topk(sc, p, topk)
+        n = int(out.count[0, i])
+        got = out.idx[0, i, :n].cpu().numpy()
+        assert np.array_equal(got, want), f"query {i}: {np.setdiff1d(got, want)[:5]} / {np.setdiff1d(want, got)[:5]}"
