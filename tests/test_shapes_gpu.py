@@ -1,0 +1,112 @@
+"""GPU parity of sparse attention on shapes the five workloads do not reach:
+batch > 1, GQA ratios 1 and 8, Vertical-Slash heads in a chunk that starts
+after key 0 (q_offset > 0), and one call that mixes token-list heads with
+Vertical-Slash, block and dense heads.  Every head is fed the oracle's own
+index set and compared with the fp64 oracle on every row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import dynamic_sparse_attention_mean_amd as dsa
+
+from parity import assert_attention_close, f64, oracle_attention_rows, oracle_head_sets, upload_sets
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def ashape(sink, local):
+    return synth.HeadPlan(dsa.VS, sink=sink, local=local, ashape=True)
+
+
+def vs(last_q, nv, ns):
+    return synth.HeadPlan(dsa.VS, last_q=last_q, nv=nv, ns=ns)
+
+
+def blk(mode, topk=0, force=False):
+    return synth.HeadPlan(dsa.BLOCK, block=64, mode=mode, topk=topk, log_alpha=-float(np.log(20.0)),
+                          force_first=force, force_diag=force)
+
+
+def dense():
+    return synth.HeadPlan(dsa.DENSE)
+
+
+def workload(seed, B, H, Hkv, Nk, heads, Nq=None):
+    Nq = Nk if Nq is None else Nq
+    q, k, v = synth.random_qkv(seed, B, H, Hkv, Nk, Nq=Nq)
+    return synth.Workload(f"shape{seed}", q, k, v, heads, q_offset=Nk - Nq)
+
+
+def run_and_check(w, what):
+    B, H, Hkv, Nq, Nk, d = w.shape
+    sets = {(b, h): oracle_head_sets(w, b, h) for b in range(B) for h in range(H)}
+    kinds, vsi, bi = upload_sets(w, sets, DEV)
+    o, lse = dsa.sparse_prefill_attn(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), kinds, vs=vsi, blk=bi,
+                                     out_dtype=dsa.OUT_F32)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    rows = list(range(Nq))
+    for (b, h) in sets:
+        ref_o, ref_l = oracle_attention_rows(w, sets, b, h, rows)
+        assert_attention_close(o[b, h], lse[b, h], ref_o, ref_l, f"{what} b={b} h={h}")
+
+
+def test_batch2_mixed_gqa_ragged():
+    heads = [ashape(16, 100), vs(64, 40, 60), blk("topk", 4, True), dense(),
+             vs(17, 25, 80), blk("thresh"), ashape(0, 64), vs(64, 0, 30)]
+    run_and_check(workload(31, 2, 8, 2, 700, heads), "B=2")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 1)])
+def test_gqa_ratios(H, Hkv):
+    kinds = [vs(64, 30, 50), dense(), blk("topk", 3), ashape(8, 90)]
+    heads = [kinds[h % 4] for h in range(H)]
+    run_and_check(workload(40 + H, 1, H, Hkv, 513, heads), f"H={H} Hkv={Hkv}")
+
+
+def test_vertical_slash_chunk_after_key0():
+    """A 320-row chunk at the end of 1280 keys (q_offset = 960): the last
+    last_q rows of the chunk score all keys, the sets are offsets from the
+    rows' absolute positions."""
+    heads = [vs(64, 50, 90), ashape(32, 200), dense(), vs(33, 10, 300)]
+    run_and_check(workload(50, 1, 4, 2, 1280, heads, Nq=320), "chunk")
+
+
+def test_token_heads_mixed_with_other_kinds():
+    """Token-list heads (one list per query, shared by those heads) next to
+    Vertical-Slash, block and dense heads in one call; some queries have an
+    empty list (O = 0, LSE = -inf)."""
+    N, cap = 600, 100
+    kinds_plan = [synth.HeadPlan(dsa.TOKEN), vs(64, 30, 40), blk("topk", 3), synth.HeadPlan(dsa.TOKEN), dense()]
+    w = workload(60, 1, 5, 5, N, kinds_plan)
+    B, H, Hkv, Nq, Nk, d = w.shape
+    g = np.random.default_rng(7)
+    lists = []
+    for i in range(Nq):
+        n = 0 if i % 97 == 5 else int(g.integers(1, min(cap, i + 1) + 1))
+        lists.append(np.sort(g.choice(i + 1, size=n, replace=False)).astype(np.int32))
+    tok = dsa.TokenIndex.empty(1, Nq, cap, DEV)
+    idx = torch.zeros(1, Nq, cap, dtype=torch.int32)
+    cnt = torch.zeros(1, Nq, dtype=torch.int32)
+    for i, L in enumerate(lists):
+        idx[0, i, :len(L)] = torch.from_numpy(L)
+        cnt[0, i] = len(L)
+    tok.idx.copy_(idx)
+    tok.count.copy_(cnt)
+    sets = {(0, h): oracle_head_sets(w, 0, h) for h in range(H) if w.heads[h].kind != dsa.TOKEN}
+    _, vsi, bi = upload_sets(w, sets, DEV)
+    kinds = [int(p.kind) for p in w.heads]
+    o, lse = dsa.sparse_prefill_attn(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), kinds, vs=vsi, blk=bi, tok=tok,
+                                     out_dtype=dsa.OUT_F32)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    rows = list(range(Nq))
+    for h in range(H):
+        if w.heads[h].kind == dsa.TOKEN:
+            ref_o, ref_l = O.attention_rows(f64(w.q[0, h]), f64(w.k[0, h]), f64(w.v[0, h]), rows, lists)
+        else:
+            ref_o, ref_l = oracle_attention_rows(w, sets, 0, h, rows)
+        assert_attention_close(o[0, h], lse[0, h], ref_o, ref_l, f"mixed-with-tokens h={h}")
