@@ -169,9 +169,27 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 // The explicit vmcnt wait at the top of each step orders a tile's DMA before
 // the reads of its stage; the "memory" clobber keeps the compiler from moving
 // LDS accesses across the issue.  The instruction has no register results.
+// M0 (the LDS base) is saved and restored around it, so the compiler's view of
+// M0 never changes.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_addr) : "memory", "m0");
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(g), "s"(lds_addr) : "memory");
+}
+// Four DMAs of 1 KB (a full tile's share of one wave) with one M0 save/restore.
+__device__ __forceinline__ void dma16x4(const char* g0, const char* g1, const char* g2, const char* g3, uint32_t l0,
+                                        uint32_t l1, uint32_t l2, uint32_t l3) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+               "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, off\n\t"
+               "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(g0), "v"(g1), "v"(g2), "v"(g3), "s"(l0), "s"(l1), "s"(l2), "s"(l3)
+               : "memory");
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -290,9 +308,9 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ base, in
                                            const int32_t* s_cols, uint32_t lds, int w, int lane, uint32_t off) {
   if (e.flags == 0) return;
   if (e.kind == 0 && e.kt * TK + TK <= Nk) {
-    const char* tb = (const char*)(base + (size_t)e.kt * TK * 128);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(tb + off + 4096 * j, lds + (4 * j + w) * 1024);
+    const char* tb = (const char*)(base + (size_t)e.kt * TK * 128) + off;
+    dma16x4(tb, tb + 4096, tb + 8192, tb + 12288, lds + w * 1024, lds + (4 + w) * 1024, lds + (8 + w) * 1024,
+            lds + (12 + w) * 1024);
     return;
   }
 #pragma unroll

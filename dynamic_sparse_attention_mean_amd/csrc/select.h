@@ -183,4 +183,172 @@ __device__ int select_threshold(const float* __restrict__ sc, int lo, int hi, fl
   return (int)total;
 }
 
+
+// Top-k over a long row in three passes (rows of 10^4 - 10^6 keys):
+//   1. histogram of the top 12 bits of the order-preserving key (4096 bins);
+//      the bin b holding the k-th largest key follows from a suffix scan;
+//   2. the keys of bin b go to LDS (key, index) and each wave counts, over its
+//      own contiguous segment, the keys above bin b;
+//   3. an LDS radix select on the low 20 bits of the candidates gives the exact
+//      k-th key T and how many keys equal to T are taken (lowest index first);
+//      the last pass writes every key > T and those keys == T in index order.
+// If bin b holds more candidates than LDS has room for, the row falls back to
+// the digit-by-digit select_topk.  Candidates are [0, n); returns the count
+// (uniform across the workgroup), writes ascending indices to out.
+constexpr int kSel3Cap = 6144;     // candidates of the threshold bin kept in LDS
+
+template <int NTH>
+struct Select3Smem {
+  union {
+    struct {
+      uint32_t hist[4096];
+      uint32_t ckey[kSel3Cap];
+      int32_t cidx[kSel3Cap];
+      uint32_t wgt[NTH / 64], weq[NTH / 64];
+      uint32_t scal[8];
+    } t;
+    SelectSmem<NTH> r;
+  };
+};
+
+template <int NTH>
+__device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int32_t* __restrict__ out,
+                                 Select3Smem<NTH>& sm) {
+  constexpr int NW = NTH / 64;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  if (k <= 0 || n <= 0) return 0;
+  if (k >= n) {                                     // every candidate
+    for (int j = tid; j < n; j += NTH) out[j] = j;
+    return n;
+  }
+  // ---- pass 1: 12-bit histogram
+  for (int i = tid; i < 4096; i += NTH) sm.t.hist[i] = 0u;
+  __syncthreads();
+  for (int j = tid; j < n; j += NTH) atomicAdd(&sm.t.hist[f32_order_key(sc[j]) >> 20], 1u);
+  __syncthreads();
+  if (w == 0) {
+    // lane l owns bins 4095 - 64 l .. 4032 - 64 l (descending)
+    uint32_t s = 0u;
+    for (int i = 0; i < 64; ++i) s += sm.t.hist[4095 - 64 * l - i];
+    const uint32_t incl = wave_incl_scan(s);
+    const uint32_t excl = incl - s;
+    if (excl < (uint32_t)k && incl >= (uint32_t)k) {
+      uint32_t run = excl;
+      for (int i = 0; i < 64; ++i) {
+        const uint32_t c = sm.t.hist[4095 - 64 * l - i];
+        if (run + c >= (uint32_t)k) {
+          sm.t.scal[0] = 4095u - 64u * l - i;   // threshold bin
+          sm.t.scal[1] = run;                   // keys above it
+          sm.t.scal[2] = c;                     // keys in it
+          break;
+        }
+        run += c;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = sm.t.scal[0], above = sm.t.scal[1], inbin = sm.t.scal[2];
+  if (inbin > (uint32_t)kSel3Cap) {
+    __syncthreads();                                // the storage is reused below
+    return select_topk<NTH>(sc, 0, n, -1, -1, k, out, sm.r);
+  }
+  // ---- pass 2: candidates of the threshold bin; keys above it per wave segment
+  const int seg = (n + NW - 1) / NW;
+  const int s0 = min(n, w * seg), s1 = min(n, (w + 1) * seg);
+  if (tid == 0) sm.t.scal[3] = 0u;
+  __syncthreads();
+  uint32_t gt = 0u;
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    uint32_t key = 0u;
+    bool g = false, c = false;
+    if (j < s1) {
+      key = f32_order_key(sc[j]);
+      g = (key >> 20) > bin;
+      c = (key >> 20) == bin;
+    }
+    gt += __popcll(__builtin_amdgcn_ballot_w64(g));
+    const uint64_t bc = __builtin_amdgcn_ballot_w64(c);
+    if (bc) {
+      uint32_t base = 0u;
+      if (l == 0) base = atomicAdd(&sm.t.scal[3], (uint32_t)__popcll(bc));
+      base = __shfl(base, 0, 64);
+      if (c) {
+        const uint32_t pos = base + ballot_rank(bc);
+        sm.t.ckey[pos] = key;
+        sm.t.cidx[pos] = j;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- exact threshold among the candidates: radix select on the low 20 bits
+  const int nc = (int)inbin;
+  uint32_t prefix = bin << 20, pmask = 0xFFF00000u;
+  int need = k - (int)above;                        // 1 <= need <= nc
+  for (int dg = 0; dg < 3; ++dg) {
+    const int sh = dg == 0 ? 12 : (dg == 1 ? 4 : 0);   // digits: bits 19-12, 11-4, 3-0
+    const uint32_t dmask = dg == 2 ? 15u : 255u;
+    for (int i = tid; i < 256; i += NTH) sm.t.hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nc; i += NTH) {
+      const uint32_t key = sm.t.ckey[i];
+      if ((key & pmask) == prefix) atomicAdd(&sm.t.hist[(key >> sh) & dmask], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t run = 0u;
+      for (int d = (int)dmask; d >= 0; --d) {
+        const uint32_t c = sm.t.hist[d];
+        if (run + c >= (uint32_t)need) {
+          sm.t.scal[4] = (uint32_t)d;
+          sm.t.scal[5] = run;
+          break;
+        }
+        run += c;
+      }
+    }
+    __syncthreads();
+    prefix |= sm.t.scal[4] << sh;
+    pmask |= dmask << sh;
+    need -= (int)sm.t.scal[5];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int need_eq = need;
+  // per-segment counts of candidates above T / equal to T
+  if (l == 0) { sm.t.wgt[w] = gt; sm.t.weq[w] = 0u; }
+  __syncthreads();
+  for (int i = tid; i < nc; i += NTH) {
+    const uint32_t key = sm.t.ckey[i];
+    const int sgi = sm.t.cidx[i] / seg;
+    if (key > T) atomicAdd(&sm.t.wgt[sgi], 1u);
+    else if (key == T) atomicAdd(&sm.t.weq[sgi], 1u);
+  }
+  __syncthreads();
+  uint32_t out_pos = 0u, eq_before = 0u;
+  for (int i = 0; i < w; ++i) {
+    const uint32_t g2 = sm.t.wgt[i], e2 = sm.t.weq[i];
+    out_pos += g2 + (uint32_t)max(0, min(need_eq - (int)eq_before, (int)e2));
+    eq_before += e2;
+  }
+  // ---- pass 3: write the selected keys of this wave's segment in index order
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + l;
+    bool g = false, e = false;
+    if (j < s1) {
+      const uint32_t key = f32_order_key(sc[j]);
+      g = key > T;
+      e = key == T;
+    }
+    const uint64_t be = __builtin_amdgcn_ballot_w64(e);
+    const bool take = g || (e && (int)(eq_before + ballot_rank(be)) < need_eq);
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(take);
+    if (take) out[out_pos + ballot_rank(bs)] = j;
+    out_pos += __popcll(bs);
+    eq_before += __popcll(be);
+  }
+  __syncthreads();
+  return k;
+}
+
 }  // namespace dsa

@@ -200,14 +200,14 @@ __global__ __launch_bounds__(1024) void vs_select_kernel(const float* v, const f
                                                          HeadList heads, int nv, int ns, int32_t* cols,
                                                          int32_t* cols_count, int cols_cap, int32_t* diags,
                                                          int32_t* diags_count, int diags_cap) {
-  __shared__ SelectSmem<1024> sm;
+  __shared__ Select3Smem<1024> sm;
   const int which = blockIdx.x, hi = blockIdx.y, b = blockIdx.z;
   const int h = heads.h[hi];
   const size_t row = (size_t)(b * heads.n + hi);
   const size_t bh = (size_t)b * H + h;
   const float* sc = (which == 0 ? v : s) + row * Nk;
   int32_t* out = which == 0 ? cols + bh * cols_cap : diags + bh * diags_cap;
-  const int n = select_topk<1024>(sc, 0, Nk, -1, -1, which == 0 ? nv : ns, out, sm);
+  const int n = select_topk_3pass<1024>(sc, Nk, which == 0 ? nv : ns, out, sm);
   if (threadIdx.x == 0) (which == 0 ? cols_count : diags_count)[bh] = n;
 }
 
