@@ -38,19 +38,29 @@ __device__ __forceinline__ void load_qfrag(const VsScoreArgs& a, int b, int h, i
   }
 }
 
-// S^T block: keys kt*64 + 32 kb + (0..31) against this wave's 32 query rows.
-__device__ __forceinline__ f32x16 score_block(const uint16_t* kp, int Nk, int kt, int kb, const Frag& f) {
+// K fragments of keys kt*64 + 32 kb + (0..31) (zero beyond Nk).
+struct KFrag {
+  u32x4 x[8];
+};
+__device__ __forceinline__ void load_kfrag(const uint16_t* kp, int Nk, int kt, int kb, KFrag& k) {
   const int l = threadIdx.x & 63, hh = l >> 5;
   const int key = kt * 64 + 32 * kb + (l & 31);
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (key < Nk) x = *(const u32x4*)(kp + (size_t)key * 128 + 16 * ks + 8 * hh);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), f.q[ks], acc, 0, 0, 0);
+    k.x[ks] = x;
   }
+}
+
+// S^T block: those keys against this wave's 32 query rows.
+__device__ __forceinline__ f32x16 score_block(const KFrag& k, const Frag& f) {
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k.x[ks]), f.q[ks], acc, 0, 0, 0);
   return acc;
 }
 
@@ -58,7 +68,7 @@ constexpr float kScale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(
 
 __global__ __launch_bounds__(256) void vs_pass1_kernel(VsScoreArgs a) {
   __shared__ float s_m[2][64], s_l[2][64];
-  const int c = blockIdx.x, hi = blockIdx.y, b = blockIdx.z;
+  const int hi = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int h = a.heads.h[hi];
   const int kvh = h / (a.H / a.Hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hh = l >> 5, qn = l & 31;
@@ -70,8 +80,12 @@ __global__ __launch_bounds__(256) void vs_pass1_kernel(VsScoreArgs a) {
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * a.Nk) * 128;
   float m = -INFINITY, s = 0.f;
   const int kt_end = min((c + 1) * CH, (a.Nk + 63) / 64);
+  KFrag kn;
+  if (c * CH < kt_end) load_kfrag(kp, a.Nk, c * CH, kb, kn);
   for (int kt = c * CH; kt < kt_end; ++kt) {
-    const f32x16 acc = score_block(kp, a.Nk, kt, kb, f);
+    const KFrag kc = kn;
+    if (kt + 1 < kt_end) load_kfrag(kp, a.Nk, kt + 1, kb, kn);   // one tile ahead
+    const f32x16 acc = score_block(kc, f);
     float z[16];
     float mt = -INFINITY;
 #pragma unroll
@@ -114,7 +128,7 @@ __global__ __launch_bounds__(256) void vs_pass2_kernel(VsScoreArgs a) {
   __shared__ float s_p[64 * 65];
   __shared__ float s_diag[DSPAN];
   __shared__ float s_mr[64], s_il[64];
-  const int c = blockIdx.x, hi = blockIdx.y, b = blockIdx.z;
+  const int hi = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int h = a.heads.h[hi];
   const int kvh = h / (a.H / a.Hkv);
   const int tid = threadIdx.x;
@@ -149,8 +163,12 @@ __global__ __launch_bounds__(256) void vs_pass2_kernel(VsScoreArgs a) {
   // offset of local diagonal slot 0 of this chunk
   const int o_min = a.Nk - a.last_q - (kt0 + CH - 1) * 64 - 63;
   float* vo = a.v_out + row * a.Nk;
+  KFrag kn;
+  if (kt0 < kt_end) load_kfrag(kp, a.Nk, kt0, kb, kn);
   for (int kt = kt0; kt < kt_end; ++kt) {
-    const f32x16 acc = score_block(kp, a.Nk, kt, kb, f);
+    const KFrag kc = kn;
+    if (kt + 1 < kt_end) load_kfrag(kp, a.Nk, kt + 1, kb, kn);   // one tile ahead
+    const f32x16 acc = score_block(kc, f);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int cc = 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
@@ -235,7 +253,7 @@ hipError_t launch_vs_scores(const VsScoreArgs& a0, hipStream_t st) {
   VsScoreArgs a = a0;
   a.chunk_tiles = CH;
   a.nchunks = ((a.Nk + 63) / 64 + CH - 1) / CH;
-  dim3 grid(a.nchunks, a.heads.n, a.B);
+  dim3 grid(a.heads.n, a.nchunks, a.B);
   hipLaunchKernelGGL(vs_pass1_kernel, grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(vs_pass2_kernel, grid, dim3(256), 0, st, a);
   const int cb = std::min(64, (a.Nk + 255) / 256);
