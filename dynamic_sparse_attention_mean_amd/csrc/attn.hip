@@ -24,11 +24,18 @@
 //  * Online softmax in fp32 (base 2, scale folded into the exponent), P rounded
 //    to bf16 for the MFMA and summed in that same rounding (v_dot2_f32_bf16), the
 //    accumulator rescaled lazily (only when the row max grows by > 8 in log2).
-//  * Vertical-Slash heads: a compile step turns the column / diagonal lists into
-//    bitmaps and the set A of key-tile offsets a crossed by a selected diagonal
-//    (pairs use A u (A+1)).  Strip tiles carry an exact per-element mask
-//    (diagonal bit | column bit, causal); columns outside all strip tiles are
-//    gathered 64 at a time.  Every selected (i, j) is visited exactly once.
+//  * Vertical-Slash heads run on a skewed schedule of 32x32 sub-blocks.  In the
+//    sub-block of 32 rows starting at position R and 32 keys starting at R - 32e
+//    every offset i - j lies in [32e - 31, 32e + 31], whatever R is; so a compile
+//    step turns the diagonal list into the set D of such e that hold a selected
+//    diagonal.  For each e in D (descending) wave w of the pair takes the 32 keys
+//    starting at P0 + 32 (w - e): all four waves have a sub-block at every step,
+//    and the block a wave uses is the one its neighbour used one step before, so
+//    a step brings in one new 32-key block of K and V (a five-slot LDS ring).
+//    Each sub-block carries the exact mask (diagonal bit | column bit, causal).
+//    Columns a wave's sub-blocks do not cover are gathered 64 at a time and the
+//    wave masks the ones it covered.  Every selected (i, j) is visited exactly
+//    once.
 //  * Persistent workgroups pull items from per-XCD queues (longest rows first)
 //    and steal from other queues when their own is empty.
 #include "common.h"
@@ -46,7 +53,7 @@ constexpr int TK = 64;       // keys per key tile
 constexpr int NT = 256;      // 4 waves: two query tiles x two 32-row halves
 constexpr int GCAP = 2048;   // gathered columns staged per round
 
-enum { M_NONE = 0, M_CAUSAL = 1, M_VS = 2, M_GATHER = 3, M_SKIP = 4 };
+enum { M_NONE = 0, M_CAUSAL = 1, M_GATHER = 3, M_SKIP = 4 };
 
 struct Sched {
   int nq;                       // number of queues
@@ -63,7 +70,7 @@ struct BhList {
 // ------------------------------------------------------------------ bitmaps
 __device__ __forceinline__ bool test_bit(const uint32_t* bm, int i) { return (bm[i >> 5] >> (i & 31)) & 1u; }
 
-// any / all bits set in [lo, hi] (inclusive, 0 <= lo <= hi) of an unpadded bitmap
+// any bit set in [lo, hi] (inclusive, 0 <= lo <= hi) of an unpadded bitmap
 __device__ bool range_any(const uint32_t* bm, int lo, int hi) {
   for (int wd = lo >> 5; wd <= (hi >> 5); ++wd) {
     uint32_t m = ~0u;
@@ -72,15 +79,6 @@ __device__ bool range_any(const uint32_t* bm, int lo, int hi) {
     if (bm[wd] & m) return true;
   }
   return false;
-}
-__device__ bool range_all(const uint32_t* bm, int lo, int hi) {
-  for (int wd = lo >> 5; wd <= (hi >> 5); ++wd) {
-    uint32_t m = ~0u;
-    if (wd == (lo >> 5)) m &= ~0u << (lo & 31);
-    if (wd == (hi >> 5)) m &= ~0u >> (31 - (hi & 31));
-    if ((bm[wd] & m) != m) return false;
-  }
-  return true;
 }
 
 // Set the bits of the listed columns (vbits) and diagonals (sbits, stored with
@@ -105,53 +103,41 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
   }
 }
 
-// Key-tile offsets a in [0, TA).  a is in A iff a selected diagonal crosses
-// some pair (query tile t, key tile t - a), i.e. offsets [64a - 63, 64a + 63]
-// hold a set bit; a >= 1 is "full" (no mask needed) iff all of them are set.
-// A query-tile pair (t, t + 1) visits key tiles t + 1 - a for a in A2 = A u (A+1);
-// A2 is written as an ascending list and as a bitmap.
-__global__ __launch_bounds__(256) void vs_tiles_kernel(AttnArgs a, BhList L, int TA) {
+// Sub-block offsets e in [0, ND): e is in D iff the offsets [32e - 31, 32e + 31]
+// hold a selected diagonal.  D is written as a bitmap, as an ascending list and
+// as the prefix counts #{e' in D : e' <= e}.
+__global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, int ND) {
   const int bh = L.bh[blockIdx.x];
   const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
-  uint32_t* fb = a.fbits + (size_t)bh * a.aw;
-  uint32_t* a2b = a.a2bits + (size_t)bh * a.aw;
-  int32_t* al = a.a2list + (size_t)bh * a.acap;
-  int32_t* ale = a.a2le + (size_t)bh * a.acap;
+  uint32_t* db = a.dbits + (size_t)bh * a.dw;
+  int32_t* dl = a.dlist + (size_t)bh * a.dcap;
+  int32_t* dle = a.dle + (size_t)bh * a.dcap;
   __shared__ int s_wave[4];
   __shared__ int s_base;
   if (threadIdx.x == 0) s_base = 0;
   __syncthreads();
   const int w = threadIdx.x >> 6;
-  auto in_a = [&](int t) {
-    if (t < 0 || t >= TA) return false;
-    const int lo = max(0, 64 * t - 63), hi = min(a.Nk - 1, 64 * t + 63);
-    return lo <= hi && range_any(sb, lo, hi);
-  };
-  for (int a0 = 0; a0 < TA; a0 += 256) {
-    const int t = a0 + threadIdx.x;
-    bool in2 = false;
-    if (t < TA) {
-      const bool inA = in_a(t);
-      in2 = inA || in_a(t - 1);
-      if (inA && t >= 1) {
-        const int lo = 64 * t - 63, hi = min(a.Nk - 1, 64 * t + 63);
-        if (lo <= hi && range_all(sb, lo, hi)) atomicOr(&fb[t >> 5], 1u << (t & 31));
-      }
-      if (in2) atomicOr(&a2b[t >> 5], 1u << (t & 31));
+  for (int e0 = 0; e0 < ND; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    bool in = false;
+    if (e < ND) {
+      const int lo = max(0, 32 * e - 31), hi = min(a.Nk - 1, 32 * e + 31);
+      in = lo <= hi && range_any(sb, lo, hi);
+      if (in) atomicOr(&db[e >> 5], 1u << (e & 31));
     }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(in2);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(in);
     const uint32_t rank = ballot_rank(bal);
     if ((threadIdx.x & 63) == 0) s_wave[w] = __popcll(bal);
     __syncthreads();
     int off = s_base;
     for (int i = 0; i < w; ++i) off += s_wave[i];
-    if (in2) al[off + rank] = t;
-    if (t < TA) ale[t] = off + rank + (in2 ? 1 : 0);     // #{a in A2 : a <= t}
+    if (in) dl[off + rank] = e;
+    if (e < ND) dle[e] = off + rank + (in ? 1 : 0);
     __syncthreads();
     if (threadIdx.x == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.a2count[bh] = s_base;
+  if (threadIdx.x == 0) a.dcount[bh] = s_base;
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -207,7 +193,6 @@ typedef const __attribute__((address_space(4))) int32_t c_i32_t;
 typedef const __attribute__((address_space(4))) uint32_t c_u32_t;
 __device__ __forceinline__ int ldc(const int32_t* p, size_t i) { return ((c_i32_t*)p)[i]; }
 __device__ __forceinline__ uint32_t ldc(const uint32_t* p, size_t i) { return ((c_u32_t*)p)[i]; }
-__device__ __forceinline__ bool test_bit_c(const uint32_t* bm, int i) { return (ldc(bm, i >> 5) >> (i & 31)) & 1u; }
 
 // One entry of a pair's tile stream.
 struct Entry {
@@ -215,15 +200,10 @@ struct Entry {
   int kt;      // key tile index, or gather chunk index
   int cnt;     // valid keys of a gather chunk
   int flags;   // bit h: query tile h of the pair uses this entry
-  int full;    // VS strip tile: bit h set if every entry is selected for query tile h
 };
 
 struct Item {
   int bh, kvh, kind, P0, last_pos, tq1;
-  // VS
-  const int32_t* a2;       // strip tile offsets (relative to tq1), ascending
-  const uint32_t* fb;      // "full" bits of tile offsets
-  int nstrip;
   // BLOCK
   const int32_t* l0;       // list of query block I0 (or of the shared block)
   const int32_t* l1;       // list of query block I0 + 1 (block 64 only)
@@ -236,7 +216,7 @@ struct Item {
 // issued while entry n is being processed (one step of prefetch).
 struct Cursor {
   int n;                   // index of the next entry
-  int raw;                 // prefetched value for entry n (VS strip / shared block list)
+  int raw;                 // prefetched value for entry n (shared block list)
   int i0, i1, x0, x1;      // two-list merge state (block 64): heads of both lists
   int x0n, x1n;            // prefetched successors of the heads
 };
@@ -248,8 +228,7 @@ __device__ __forceinline__ void cursor_init(const Item& it, Cursor& c) {
   c.raw = 0;
   c.i0 = c.i1 = 0;
   c.x0 = c.x1 = c.x0n = c.x1n = 0x7fffffff;
-  if (it.kind == 1) c.raw = it.nstrip > 0 ? ldc(it.a2, 0) : 0;
-  else if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? ldc(it.l0, 0) : 0;
+  if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? ldc(it.l0, 0) : 0;
   else if (it.kind == 2) {
     c.x0 = list_at(it.l0, it.n0, 0); c.x1 = list_at(it.l1, it.n1, 0);
     c.x0n = list_at(it.l0, it.n0, 1); c.x1n = list_at(it.l1, it.n1, 1);
@@ -267,21 +246,11 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   e.cnt = 0;
   e.flags = 3;
   e.kind = 0;
-  e.full = 0;
   const int n = c.n++;
   if (it.kind == 1) {
-    if (n < it.nstrip) {
-      // tile offset of query tile h of the pair is raw - 1 + h; offsets >= 1 may be full
-      const int r = c.raw;
-      e.kt = it.tq1 - r;
-      if (r >= 2 && test_bit_c(it.fb, r - 1)) e.full |= 1;
-      if (r >= 1 && test_bit_c(it.fb, r)) e.full |= 2;
-      c.raw = (n + 1 < it.nstrip) ? ldc(it.a2, n + 1) : 0;
-    } else {
-      e.kind = 1;
-      e.kt = n - it.nstrip;
-      e.cnt = min(TK, it.ngather - e.kt * TK);
-    }
+    e.kind = 1;
+    e.kt = n;
+    e.cnt = min(TK, it.ngather - n * TK);
   } else if (it.kind == 2 && it.per == 2) {
     e.kt = c.raw * 2 + (n & 1);
     if (n & 1) c.raw = ((n >> 1) + 1 < it.n0) ? ldc(it.l0, (n >> 1) + 1) : 0;
@@ -344,11 +313,27 @@ __device__ __forceinline__ uint32_t causal_mask32(int top) {   // bits c <= top
 #define DSA_PRIO_LO() ((void)0)
 #endif
 
+// LDS arena of one workgroup.  The five-slot ring of 32-key K/V blocks used by
+// the Vertical-Slash sub-block steps covers all of it; the two-stage ring of
+// 64-key tiles, the gathered column list, its coverage bytes and a few shared
+// counters are laid out inside it for the other phases.  80 KB: two workgroups
+// fill the 160 KB of a CU.
+constexpr int NSLOT = 5;
+constexpr int SLOT = 2 * 32 * 256;                 // K [32 rows][256 B], then V
+constexpr int LDS_BYTES = NSLOT * SLOT;
+constexpr int OFF_COLS = 2 * 2 * TK * 256;         // after the 64-key ring [stage][K, V]
+constexpr int OFF_COV = OFF_COLS + GCAP * 4;
+constexpr int OFF_MISC = OFF_COV + GCAP;
+static_assert(OFF_MISC + 8 * 4 <= LDS_BYTES, "LDS arena overflow");
+
+__device__ __forceinline__ int mod5(int u) { return ((u % NSLOT) + NSLOT) % NSLOT; }
+
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_SIMD))) void attn_kernel(
     const AttnArgs a, const Sched sc) {
-  __shared__ __align__(1024) char s_kv[2][2][TK * 256];   // [stage][0 = K, 1 = V]
-  __shared__ int32_t s_cols[GCAP];
-  __shared__ int s_misc[8];
+  __shared__ __align__(1024) char s_lds[LDS_BYTES];
+  int32_t* const s_cols = (int32_t*)(s_lds + OFF_COLS);
+  uint8_t* const s_cov = (uint8_t*)(s_lds + OFF_COV);
+  int* const s_misc = (int*)(s_lds + OFF_MISC);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -365,10 +350,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
   const uint32_t off_v = rl * 256 + (((l & 15) ^ ((rl & 3) << 2)) * 16);
   // lane-constant parts of the V fragment addresses
   const int G = l >> 4, si = l & 15;
-  const int v_row0 = 4 * (G >> 1) + (si >> 2);           // + 32 kb + 16 s2 (+ 8)
+  const int v_row0 = 4 * (G >> 1) + (si >> 2);           // + 16 s2 (+ 8)
   const int v_half = (si & 1) * 8;
-  // LDS byte address of the ring; stage s, K (0) or V (1) at + (2 s + kv) * 16 KB
-  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)&s_kv[0][0][0]);
+  // LDS byte address of the arena (64-key ring: stage s, K (0) or V (1) at + (2 s + kv) * 16 KB)
+  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)&s_lds[0]);
 
   for (int qi = 0; qi < sc.nq; ++qi) {
     const int g = (myq + qi) % sc.nq;
@@ -392,12 +377,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       it.P0 = r0 + a.q_offset;
       it.last_pos = min(a.Nq, r0 + 2 * TQ) - 1 + a.q_offset;
       it.tq1 = it.P0 / TK + 1;
-      it.nstrip = 0;
       it.ngather = 0;
       it.per = 1;
       it.n0 = it.n1 = 0;
-      it.a2 = nullptr;
-      it.fb = nullptr;
       it.l0 = it.l1 = nullptr;
 
       const uint16_t* kbp = a.k + ((size_t)(b * a.Hkv + it.kvh) * a.Nk) * 128;
@@ -428,16 +410,190 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
-      const uint32_t* sbits = nullptr;
-      const uint32_t* vbits = nullptr;
+      // One 32x32 sub-block: S^T = K Q^T over the 32 keys whose swizzled K rows
+      // start at kbase, online softmax under the mask M (bit c <-> key c of this
+      // lane's row), O^T += V^T P^T with the V rows at vbase.
+      auto sub32 = [&](const char* kbase, const lds_char_t* vbase, uint32_t M) {
+        if (!row_ok) M = 0u;
+        if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) return;
+        const bool masked = __builtin_amdgcn_ballot_w64(M != ~0u) != 0;
+
+        // ---- S^T = K Q^T for these 32 keys (eight K fragments read first)
+        f32x16 sacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+        u32x4 kf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(kbase + qn * 256 + swz_k(qn, 2 * ks + hh) * 16);
+        DSA_PRIO_HI();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        DSA_PRIO_LO();
+
+        // ---- mask (one wave-uniform branch), online softmax on raw scores
+        // (the scale is folded into exp2)
+        if (masked) {
+          const uint32_t mk = M >> (4 * hh);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int pos = 8 * (v >> 2) + (v & 3);
+            const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
+            sacc[v] = __uint_as_float((__float_as_uint(sacc[v]) & keep) | (0xff800000u & ~keep));
+          }
+        }
+        float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sacc[v]), sacc[v + 1]);
+        mx = fmaxf(mx, sacc[15]);
+        {
+          // rows live in lanes l and l ^ 32: swap halves and take the max
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+        }
+        const bool grow = mx > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float mnew = grow ? mx : m_run;
+          const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
+          l_run *= f;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] *= f;
+          m_run = mnew;
+        }
+        const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        uint32_t pk[8];
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], scale2, -muse));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], scale2, -muse));
+          const uint32_t pb = pack_bf16x2(p0, p1);
+          // the row sum uses the same bf16-rounded weights as the PV product
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
+          pk[v >> 1] = pb;
+        }
+
+        // ---- O^T += V^T P^T over these 32 keys (two 16-key steps)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
+          const int rowa = 16 * s2 + v_row0;
+          const int rowb = rowa + 8;
+          short4_t ya[4], yb[4];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int cch = 4 * db + 2 * (G & 1) + ((si & 3) >> 1);
+            ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4_t*)(vbase + rowa * 256 + swz_v(rowa, cch) * 16 + v_half));
+            yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4_t*)(vbase + rowb * 256 + swz_v(rowb, cch) * 16 + v_half));
+          }
+          DSA_PRIO_HI();
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const short8_t ab = {ya[db][0], ya[db][1], ya[db][2], ya[db][3], yb[db][0], yb[db][1], yb[db][2], yb[db][3]};
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+          DSA_PRIO_LO();
+        }
+      };
+
       int gcursor = 0, gcount = 0;
+      const uint32_t* dbits = nullptr;
       if (it.kind == 1) {
-        it.a2 = a.a2list + (size_t)it.bh * a.acap;
-        it.fb = a.fbits + (size_t)it.bh * a.aw;
-        sbits = a.sbits + (size_t)it.bh * a.sw;
-        vbits = a.vbits + (size_t)it.bh * a.vw;
-        it.nstrip = ldc(a.a2le, (size_t)it.bh * a.acap + it.tq1);
+        dbits = a.dbits + (size_t)it.bh * a.dw;
         gcount = min(ldc(a.cols_count, it.bh), a.cols_cap);
+        // the arena is reused below: every wave has read the item number
+        __syncthreads();
+
+        // ---- Vertical-Slash sub-block steps.  Block u holds the 32 keys from
+        // P0 + 32 u in ring slot u mod 5; the step for offset e gives wave w the
+        // block w - e.  e runs down D (keys ascend), so consecutive e bring in
+        // one new block, which is loaded one step ahead into the free slot; the
+        // blocks of a step after a gap in D that could not go ahead are loaded at
+        // its start.
+        const uint32_t* sbits = a.sbits + (size_t)it.bh * a.sw;
+        const uint32_t* vbits = a.vbits + (size_t)it.bh * a.vw;
+        const int32_t* dl = a.dlist + (size_t)it.bh * a.dcap;
+        const int emax = min(3 + (it.P0 + 31) / 32, a.dcap - 1);   // wave 3's block still has a key >= 0
+        int k = ldc(a.dle, (size_t)it.bh * a.dcap + emax) - 1;
+        auto issue_block = [&](int u) {
+          const int k0 = it.P0 + 32 * u;
+          const uint32_t lb = ring + (uint32_t)(mod5(u) * SLOT);
+          if (k0 >= 0 && k0 + 32 <= a.Nk) {
+            const char* kb = (const char*)(kbp + (size_t)k0 * 128);
+            const char* vb = (const char*)(vbp + (size_t)k0 * 128);
+            dma16x4(kb + off_k, kb + off_k + 4096, vb + off_v, vb + off_v + 4096, lb + w * 1024,
+                    lb + (4 + w) * 1024, lb + 8192 + w * 1024, lb + 8192 + (4 + w) * 1024);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int r = 16 * j + rl;
+              const int key = min(max(k0 + r, 0), a.Nk - 1);
+              dma16(kbp + (size_t)key * 128 + swz_k(r, l & 15) * 8, lb + (4 * j + w) * 1024);
+              dma16(vbp + (size_t)key * 128 + swz_v(r, l & 15) * 8, lb + 8192 + (4 * j + w) * 1024);
+            }
+          }
+        };
+        if (k >= 0) {
+          int ec = ldc(dl, k);
+          for (int u = -ec; u <= 3 - ec; ++u) issue_block(u);
+          int ep = -1;
+          const bool wave_on = R0w <= it.last_pos;
+          while (true) {
+            const int en = k > 0 ? ldc(dl, k - 1) : -1;
+            const int u = w - ec;
+            const int k0 = it.P0 + 32 * u;
+            const bool active = wave_on && k0 + 31 >= 0;
+            // diagonal words (offsets [32 ec - 32, 32 ec + 31]) and this block's column words
+            uint32_t D0 = 0u, D1 = 0u, C0 = 0u, C1 = 0u;
+            if (active) {
+              D0 = ldc(sbits, ec + 1);
+              D1 = ldc(sbits, ec + 2);
+              C0 = ldc(vbits, max(k0, 0) >> 5);
+              C1 = k0 >= 0 ? ldc(vbits, (k0 >> 5) + 1) : 0u;
+            }
+            wait_vm();
+            __syncthreads();                     // this step's blocks landed; the previous step is done
+            if (ep >= 0) {
+              bool late = false;
+              for (int v = max(-ec, 4 - ep); v <= 3 - ec; ++v)
+                if (mod5(v - (4 - ep)) != 0) { issue_block(v); late = true; }
+              if (late) {
+                wait_vm();
+                __syncthreads();
+              }
+            }
+            if (en >= 0) {
+              for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
+                if (mod5(v - (4 - ec)) == 0) issue_block(v);
+            }
+            if (active) {
+              // lane row r sees offsets 32 ec + r - c for keys c = 0..31
+              const uint64_t dwin = ((uint64_t)D1 << 32) | D0;
+              uint32_t M = __builtin_bitreverse32((uint32_t)(dwin >> (1 + qn)));
+              if (k0 >= 0) {
+                M |= (uint32_t)((((uint64_t)C1 << 32) | C0) >> (k0 & 31));
+              } else {
+                M = (M | (C0 << (-k0))) & (~0u << (-k0));
+              }
+              if (ec == 0) M &= causal_mask32(qn);
+              const int sl = mod5(u);
+              sub32(s_lds + sl * SLOT, (const lds_char_t*)(s_lds + sl * SLOT + 8192), M);
+            }
+            if (--k < 0) break;
+            ep = ec;
+            ec = en;
+          }
+        }
+        __syncthreads();                         // the slots are free for the gather phase
       } else if (it.kind == 2) {
         it.per = a.block / TK;
         const int I0 = it.P0 / a.block;
@@ -450,19 +606,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         }
       }
 
-      for (int round = 0;; ++round) {
+      for (;;) {
         if (it.kind == 1) {
-          // stage this pair's columns: 0 <= j <= last_pos and outside every strip tile
+          // stage this pair's columns j <= last_pos, except those every wave's
+          // sub-blocks already cover; cov bit w marks a column wave w covered
+          // (or one after all of wave w's rows)
           const int32_t* cols = a.cols + (size_t)it.bh * a.cols_cap;
-          const uint32_t* a2b = a.a2bits + (size_t)it.bh * a.aw;
           int staged = 0;
           while (gcursor < gcount && staged <= GCAP - NT) {
             const int idx = gcursor + tid;
             bool keep = false;
             int j = 0;
+            uint32_t cov = 0xFu;
             if (idx < gcount) {
               j = cols[idx];
-              keep = (j >= 0) && (j <= it.last_pos) && !test_bit(a2b, it.tq1 - (j >> 6));
+              if (j >= 0 && j <= it.last_pos) {
+                const int uj = (j - it.P0) >> 5;      // floor division
+                cov = 0u;
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                  const int e = w4 - uj;
+                  const bool c = e < 0 || it.P0 + 32 * w4 > it.last_pos || (e < a.dcap && test_bit(dbits, e));
+                  cov |= (c ? 1u : 0u) << w4;
+                }
+                keep = cov != 0xFu;
+              }
             }
             const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
             __syncthreads();
@@ -470,7 +638,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             __syncthreads();
             int off = staged;
             for (int i = 0; i < w; ++i) off += s_misc[1 + i];
-            if (keep) s_cols[off + ballot_rank(bal)] = j;
+            if (keep) {
+              s_cols[off + ballot_rank(bal)] = j;
+              s_cov[off + ballot_rank(bal)] = (uint8_t)cov;
+            }
             staged += s_misc[1] + s_misc[2] + s_misc[3] + s_misc[4];
             gcursor += NT;
             const int lastc = cols[min(gcursor, gcount) - 1];
@@ -478,8 +649,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
           __syncthreads();
           it.ngather = staged;
-          if (round > 0) it.nstrip = 0;
-          it.nent = it.nstrip + (staged + TK - 1) / TK;
+          it.nent = (staged + TK - 1) / TK;
         } else if (it.kind == 2) {
           // per == 2: one shared list; per == 1: the cursor merges two lists and
           // stops when both are exhausted (nent is only an upper bound)
@@ -493,7 +663,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         Entry cur;
         cur.kind = -1;
         cur.flags = 0;
-        cur.full = 0;
         bool have = cursor_has_next(it, cc);
         if (have) {
           cur = cursor_next(it, cc);
@@ -510,41 +679,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           if (!((cur.flags >> ih) & 1) || (cur.kind == 0 && cur.kt * TK > P0w + TQ - 1) || R0w > it.last_pos)
             mode = M_SKIP;
           else if (cur.kind == 1) mode = M_GATHER;
-          else if (it.kind == 1) mode = ((cur.full >> ih) & 1) ? M_NONE : M_VS;
           else mode = (cur.kt * TK + TK - 1 > P0w) ? M_CAUSAL : M_NONE;
-          // diagonal-bitmap words covering this wave's windows and the tile's
-          // column bits (scalar loads, issued before the wait)
-          uint32_t W0 = 0u, W1 = 0u, W2 = 0u, W3 = 0u, mv0 = 0u, mv1 = 0u;
-          int wbase = 0;
-          if (mode == M_VS) {
-            wbase = R0w - cur.kt * TK - 63;               // window start of this wave's row 0 (>= -63)
-            const uint32_t* swp = sbits + ((wbase >> 5) + 2);
-            W0 = ldc(swp, 0); W1 = ldc(swp, 1); W2 = ldc(swp, 2); W3 = ldc(swp, 3);
-            mv0 = ldc(vbits, 2 * cur.kt); mv1 = ldc(vbits, 2 * cur.kt + 1);
-          }
           wait_vm();
           __syncthreads();                       // tile n landed; every wave is done with tile n - 1
           Entry nxt;
           nxt.kind = -1;
           nxt.flags = 0;
-          nxt.full = 0;
           const bool have_n = cursor_has_next(it, cc);
           if (have_n) {
             nxt = cursor_next(it, cc);
             issue_tile<false>(kbp, a.Nk, nxt, s_cols, ring + (stage ^ 1) * 2 * TK * 256, w, l, off_k);
             issue_tile<true>(vbp, a.Nk, nxt, s_cols, ring + ((stage ^ 1) * 2 + 1) * TK * 256, w, l, off_v);
           }
-          const char* sk = s_kv[stage][0];
-          const lds_char_t* sv = (const lds_char_t*)s_kv[stage][1];
-
-          // 64-bit window of diagonal bits for this lane's row (bit b <-> offset lo + b)
-          uint64_t swin = 0;
-          if (mode == M_VS) {
-            const int sh = (wbase & 31) + qn;            // 0 .. 62
-            const uint64_t lo64 = ((uint64_t)W1 << 32) | W0;
-            const uint64_t hi64 = ((uint64_t)W3 << 32) | W2;
-            swin = sh ? ((lo64 >> sh) | (hi64 << (64 - sh))) : lo64;
-          }
+          const char* sk = s_lds + stage * 2 * TK * 256;
+          const lds_char_t* sv = (const lds_char_t*)(s_lds + (stage * 2 + 1) * TK * 256);
 
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
@@ -555,10 +703,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               M = 0u;
             } else if (mode == M_CAUSAL) {
               M = causal_mask32(ktop);
-            } else if (mode == M_VS) {
-              // key c of this half sits at window bit 63 - 32 kb - c
-              const uint32_t part = kb == 0 ? (uint32_t)(swin >> 32) : (uint32_t)swin;
-              M = (__builtin_bitreverse32(part) | (kb == 0 ? mv0 : mv1)) & causal_mask32(ktop);
             } else if (mode == M_GATHER) {
               // staged columns ascend: the keys <= iq are a prefix of the chunk
               const int base = cur.kt * TK + 32 * kb;
@@ -573,97 +717,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
                 }
                 M = lo >= 32 ? ~0u : ((1u << lo) - 1u);
               }
+              // columns this wave's sub-blocks already visited
+              const bool ex = (s_cov[base + (l & 31)] >> w) & 1u;
+              M &= ~(uint32_t)__builtin_amdgcn_ballot_w64(ex);
             }
-            if (!row_ok) M = 0u;
-            if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) continue;
-            const bool masked = __builtin_amdgcn_ballot_w64(M != ~0u) != 0;
-
-            // ---- S^T = K Q^T for these 32 keys (eight K fragments read first)
-            f32x16 sacc;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-            const int row = 32 * kb + qn;
-            u32x4 kf[8];
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(sk + row * 256 + swz_k(row, 2 * ks + hh) * 16);
-            DSA_PRIO_HI();
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sacc, 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            DSA_PRIO_LO();
-
-            // ---- mask (one wave-uniform branch), online softmax on raw scores
-            // (the scale is folded into exp2)
-            if (masked) {
-              const uint32_t mk = M >> (4 * hh);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int pos = 8 * (v >> 2) + (v & 3);
-                const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
-                sacc[v] = __uint_as_float((__float_as_uint(sacc[v]) & keep) | (0xff800000u & ~keep));
-              }
-            }
-            float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-            for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sacc[v]), sacc[v + 1]);
-            mx = fmaxf(mx, sacc[15]);
-            {
-              // rows live in lanes l and l ^ 32: swap halves and take the max
-              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-              mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
-            }
-            const bool grow = mx > m_run + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-              const float mnew = grow ? mx : m_run;
-              const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
-              l_run *= f;
-#pragma unroll
-              for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[db][v] *= f;
-              m_run = mnew;
-            }
-            const float muse = (m_run == -INFINITY) ? 0.f : m_run;
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-            uint32_t pk[8];
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], scale2, -muse));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], scale2, -muse));
-              const uint32_t pb = pack_bf16x2(p0, p1);
-              // the row sum uses the same bf16-rounded weights as the PV product
-              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
-              pk[v >> 1] = pb;
-            }
-
-            // ---- O^T += V^T P^T over these 32 keys (two 16-key steps)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
-              const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
-              const int rowa = 32 * kb + 16 * s2 + v_row0;
-              const int rowb = rowa + 8;
-              short4_t ya[4], yb[4];
-#pragma unroll
-              for (int db = 0; db < 4; ++db) {
-                const int cch = 4 * db + 2 * (G & 1) + ((si & 3) >> 1);
-                ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(sv + rowa * 256 + swz_v(rowa, cch) * 16 + v_half));
-                yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4_t*)(sv + rowb * 256 + swz_v(rowb, cch) * 16 + v_half));
-              }
-              DSA_PRIO_HI();
-#pragma unroll
-              for (int db = 0; db < 4; ++db) {
-                const short8_t ab = {ya[db][0], ya[db][1], ya[db][2], ya[db][3], yb[db][0], yb[db][1], yb[db][2], yb[db][3]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
-              }
-              __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-              __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-              DSA_PRIO_LO();
-            }
+            sub32(sk + 32 * kb * 256, sv + 32 * kb * 256, M);
           }
           cur = nxt;
           have = have_n;
@@ -721,28 +779,26 @@ int cu_count() {
 }
 
 struct VsLayout {
-  int sw, vw, aw, acap, TA;
-  size_t off_s, off_v, off_f, off_a2, off_ac, off_ctr, off_al, off_ale, total_words;
+  int sw, vw, dw, ND;
+  size_t off_s, off_v, off_d, off_dc, off_ctr, off_dl, off_dle, total_words;
 };
 
 VsLayout vs_layout(int B, int H, int Nk) {
   VsLayout L;
   L.sw = (Nk + 31) / 32 + 5;
   L.vw = (Nk + 31) / 32 + 2;
-  L.TA = (Nk + TK - 1) / TK + 2;
-  L.aw = (L.TA + 31) / 32 + 1;
-  L.acap = L.TA;
+  L.ND = (Nk + 30) / 32 + 1;     // e with 32e - 31 <= Nk - 1
+  L.dw = (L.ND + 31) / 32 + 1;
   const size_t nbh = (size_t)B * H;
   size_t off = 0;
   L.off_ctr = off; off += 64;
   L.off_s = off; off += nbh * L.sw;
   L.off_v = off; off += nbh * L.vw;
-  L.off_f = off; off += nbh * L.aw;
-  L.off_a2 = off; off += nbh * L.aw;
-  L.off_ac = off; off += nbh;
+  L.off_d = off; off += nbh * L.dw;
+  L.off_dc = off; off += nbh;
   L.total_words = off;          // region zeroed before every call
-  L.off_al = off; off += nbh * L.acap;
-  L.off_ale = off; off += nbh * L.acap;
+  L.off_dl = off; off += nbh * L.ND;
+  L.off_dle = off; off += nbh * L.ND;
   (void)off;
   return L;
 }
@@ -751,7 +807,7 @@ VsLayout vs_layout(int B, int H, int Nk) {
 
 size_t attn_workspace_bytes(int B, int H, int Nk) {
   VsLayout L = vs_layout(B, H, Nk);
-  return (L.off_ale + (size_t)B * H * L.acap) * 4 + 256;
+  return (L.off_dle + (size_t)B * H * L.ND) * 4 + 256;
 }
 
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
@@ -769,12 +825,11 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   a.counters = (int32_t*)(base + L.off_ctr);
   a.sbits = base + L.off_s;
   a.vbits = base + L.off_v;
-  a.fbits = base + L.off_f;
-  a.a2bits = base + L.off_a2;
-  a.a2count = (int32_t*)(base + L.off_ac);
-  a.a2list = (int32_t*)(base + L.off_al);
-  a.a2le = (int32_t*)(base + L.off_ale);
-  a.sw = L.sw; a.vw = L.vw; a.aw = L.aw; a.acap = L.acap;
+  a.dbits = base + L.off_d;
+  a.dcount = (int32_t*)(base + L.off_dc);
+  a.dlist = (int32_t*)(base + L.off_dl);
+  a.dle = (int32_t*)(base + L.off_dle);
+  a.sw = L.sw; a.vw = L.vw; a.dw = L.dw; a.dcap = L.ND;
 
   hipError_t e = launch_zero_u32(base, L.total_words, st);
   if (e != hipSuccess) return e;
@@ -787,7 +842,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
       if (a.kind[h] == 1) vs.bh[vs.n++] = (int16_t)(b * a.H + h);
   if (vs.n > 0) {
     hipLaunchKernelGGL(vs_setbits_kernel, dim3(8, vs.n), dim3(256), 0, st, a, vs);
-    hipLaunchKernelGGL(vs_tiles_kernel, dim3(vs.n), dim3(256), 0, st, a, vs, L.TA);
+    hipLaunchKernelGGL(vs_dsteps_kernel, dim3(vs.n), dim3(256), 0, st, a, vs, L.ND);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 

@@ -69,9 +69,10 @@ struct AttnArgs {
   // Vertical-Slash sets and their compiled form (workspace)
   const int32_t* cols; const int32_t* cols_count; int cols_cap;
   const int32_t* diags; const int32_t* diags_count; int diags_cap;
-  uint32_t* sbits; uint32_t* vbits; uint32_t* abits; uint32_t* fbits; uint32_t* a2bits;
-  int32_t* a2list; int32_t* a2count; int32_t* a2le;   // A2 list, its size, #{a in A2 : a <= t}
-  int sw, vw, aw, acap;              // words per head of each bitmap; a2list capacity
+  uint32_t* sbits; uint32_t* vbits;  // diagonal bitmap (two leading pad words), column bitmap
+  uint32_t* dbits;                   // bit e set iff a selected diagonal lies in [32e - 31, 32e + 31]
+  int32_t* dlist; int32_t* dcount; int32_t* dle;   // those e ascending, their number, #{e' <= e}
+  int sw, vw, dw, dcap;              // words per head of each bitmap; dlist capacity
   // Block sets
   const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
   // Token sets
