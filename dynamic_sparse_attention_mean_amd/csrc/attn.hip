@@ -35,7 +35,10 @@
 //    Each sub-block carries the exact mask (diagonal bit | column bit, causal).
 //    Columns a wave's sub-blocks do not cover are gathered 64 at a time and the
 //    wave masks the ones it covered.  Every selected (i, j) is visited exactly
-//    once.
+//    once.  A head whose sets are exactly a sink [0, S) of columns and the
+//    diagonals [0, L) (the A-shape sets) is recognised by the compile step and
+//    runs like a dense head over the 64-key tiles of the sink and the window,
+//    with a closed-form mask on the edge tiles.
 //  * Persistent workgroups pull items from per-XCD queues (longest rows first)
 //    and steal from other queues when their own is empty.
 #include "common.h"
@@ -53,7 +56,7 @@ constexpr int TK = 64;       // keys per key tile
 constexpr int NT = 256;      // 4 waves: two query tiles x two 32-row halves
 constexpr int GCAP = 2048;   // gathered columns staged per round
 
-enum { M_NONE = 0, M_CAUSAL = 1, M_GATHER = 3, M_SKIP = 4 };
+enum { M_NONE = 0, M_CAUSAL = 1, M_WIN = 2, M_GATHER = 3, M_SKIP = 4 };
 
 struct Sched {
   int nq;                       // number of queues
@@ -105,7 +108,9 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
 
 // Sub-block offsets e in [0, ND): e is in D iff the offsets [32e - 31, 32e + 31]
 // hold a selected diagonal.  D is written as a bitmap, as an ascending list and
-// as the prefix counts #{e' in D : e' <= e}.
+// as the prefix counts #{e' in D : e' <= e}.  A head whose lists are exactly
+// cols = [0, S) and diags = [0, L) (the A-shape sets: sink S, local window L)
+// is marked as a window head: its mask is closed-form and runs on whole tiles.
 __global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, int ND) {
   const int bh = L.bh[blockIdx.x];
   const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
@@ -114,8 +119,26 @@ __global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, in
   int32_t* dle = a.dle + (size_t)bh * a.dcap;
   __shared__ int s_wave[4];
   __shared__ int s_base;
-  if (threadIdx.x == 0) s_base = 0;
+  __shared__ int s_prefix;
+  if (threadIdx.x == 0) {
+    s_base = 0;
+    s_prefix = 1;
+  }
   __syncthreads();
+  {
+    const int nc = min(a.cols_count[bh], a.cols_cap), nd = min(a.diags_count[bh], a.diags_cap);
+    const int32_t* cols = a.cols + (size_t)bh * a.cols_cap;
+    const int32_t* diags = a.diags + (size_t)bh * a.diags_cap;
+    bool ok = true;
+    for (int i = threadIdx.x; i < nc; i += 256) ok = ok && cols[i] == i;
+    for (int i = threadIdx.x; i < nd; i += 256) ok = ok && diags[i] == i;
+    if (!ok) s_prefix = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      a.win[2 * bh] = s_prefix ? nd : -1;
+      a.win[2 * bh + 1] = nc;
+    }
+  }
   const int w = threadIdx.x >> 6;
   for (int e0 = 0; e0 < ND; e0 += 256) {
     const int e = e0 + threadIdx.x;
@@ -204,6 +227,8 @@ struct Entry {
 
 struct Item {
   int bh, kvh, kind, P0, last_pos, tq1;
+  // WINDOW (kind 3): tiles [0, n0) then n1, n1 + 1, ...; sink wsink, window wlen
+  int wsink, wlen;
   // BLOCK
   const int32_t* l0;       // list of query block I0 (or of the shared block)
   const int32_t* l1;       // list of query block I0 + 1 (block 64 only)
@@ -260,6 +285,8 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
     e.flags = (c.x0 == x ? 1 : 0) | (c.x1 == x ? 2 : 0);
     if (c.x0 == x) { ++c.i0; c.x0 = c.x0n; c.x0n = list_at(it.l0, it.n0, c.i0 + 1); }
     if (c.x1 == x) { ++c.i1; c.x1 = c.x1n; c.x1n = list_at(it.l1, it.n1, c.i1 + 1); }
+  } else if (it.kind == 3) {
+    e.kt = n < it.n0 ? n : it.n1 + (n - it.n0);
   } else {
     e.kt = n;
   }
@@ -507,7 +534,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
 
       int gcursor = 0, gcount = 0;
       const uint32_t* dbits = nullptr;
-      if (it.kind == 1) {
+      if (it.kind == 1 && ldc(a.win, 2 * (size_t)it.bh) >= 0) {
+        // window head: key tiles of the sink [0, S) and of the window
+        // [P0 - L + 1, last_pos], merged when they meet
+        it.kind = 3;
+        it.wlen = ldc(a.win, 2 * (size_t)it.bh);
+        it.wsink = ldc(a.win, 2 * (size_t)it.bh + 1);
+        const int tw0 = max(0, it.P0 - it.wlen + 1) / TK;
+        const int tend = it.last_pos / TK + 1;
+        const int ts = (min(it.wsink, it.last_pos + 1) + TK - 1) / TK;     // sink tiles [0, ts)
+        if (it.wlen == 0) {
+          it.n0 = ts;
+          it.n1 = ts;
+          it.nent = ts;
+        } else if (ts >= tw0) {
+          it.n0 = 0;
+          it.n1 = 0;
+          it.nent = tend;
+        } else {
+          it.n0 = ts;
+          it.n1 = tw0;
+          it.nent = ts + (tend - tw0);
+        }
+      } else if (it.kind == 1) {
         dbits = a.dbits + (size_t)it.bh * a.dw;
         gcount = min(ldc(a.cols_count, it.bh), a.cols_cap);
         // the arena is reused below: every wave has read the item number
@@ -654,7 +703,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           // per == 2: one shared list; per == 1: the cursor merges two lists and
           // stops when both are exhausted (nent is only an upper bound)
           it.nent = it.per == 2 ? 2 * it.n0 : it.n0 + it.n1;
-        } else {
+        } else if (it.kind == 0) {
           it.nent = it.last_pos / TK + 1;
         }
 
@@ -679,6 +728,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           if (!((cur.flags >> ih) & 1) || (cur.kind == 0 && cur.kt * TK > P0w + TQ - 1) || R0w > it.last_pos)
             mode = M_SKIP;
           else if (cur.kind == 1) mode = M_GATHER;
+          else if (it.kind == 3)
+            // unmasked if every key is causal and inside the window or the sink for all the wave's rows
+            mode = (cur.kt * TK + TK - 1 <= R0w && (R0w + 31 - cur.kt * TK <= it.wlen - 1 || cur.kt * TK + TK <= it.wsink))
+                       ? M_NONE : M_WIN;
           else mode = (cur.kt * TK + TK - 1 > P0w) ? M_CAUSAL : M_NONE;
           wait_vm();
           __syncthreads();                       // tile n landed; every wave is done with tile n - 1
@@ -703,6 +756,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               M = 0u;
             } else if (mode == M_CAUSAL) {
               M = causal_mask32(ktop);
+            } else if (mode == M_WIN) {
+              // keys c <= ktop, and c >= ktop - (L - 1) (window) or below the sink
+              const int c0 = ktop - it.wlen + 1;
+              const uint32_t inwin = c0 <= 0 ? ~0u : (c0 >= 32 ? 0u : (~0u << c0));
+              const int cs = it.wsink - (cur.kt * TK + 32 * kb);
+              const uint32_t insink = cs >= 32 ? ~0u : (cs <= 0 ? 0u : ((1u << cs) - 1u));
+              M = causal_mask32(ktop) & (inwin | insink);
             } else if (mode == M_GATHER) {
               // staged columns ascend: the keys <= iq are a prefix of the chunk
               const int base = cur.kt * TK + 32 * kb;
@@ -780,7 +840,7 @@ int cu_count() {
 
 struct VsLayout {
   int sw, vw, dw, ND;
-  size_t off_s, off_v, off_d, off_dc, off_ctr, off_dl, off_dle, total_words;
+  size_t off_s, off_v, off_d, off_dc, off_ctr, off_dl, off_dle, off_win, total_words;
 };
 
 VsLayout vs_layout(int B, int H, int Nk) {
@@ -799,6 +859,7 @@ VsLayout vs_layout(int B, int H, int Nk) {
   L.total_words = off;          // region zeroed before every call
   L.off_dl = off; off += nbh * L.ND;
   L.off_dle = off; off += nbh * L.ND;
+  L.off_win = off; off += nbh * 2;
   (void)off;
   return L;
 }
@@ -807,7 +868,7 @@ VsLayout vs_layout(int B, int H, int Nk) {
 
 size_t attn_workspace_bytes(int B, int H, int Nk) {
   VsLayout L = vs_layout(B, H, Nk);
-  return (L.off_dle + (size_t)B * H * L.ND) * 4 + 256;
+  return (L.off_win + (size_t)B * H * 2) * 4 + 256;
 }
 
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
@@ -829,6 +890,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   a.dcount = (int32_t*)(base + L.off_dc);
   a.dlist = (int32_t*)(base + L.off_dl);
   a.dle = (int32_t*)(base + L.off_dle);
+  a.win = (int32_t*)(base + L.off_win);
   a.sw = L.sw; a.vw = L.vw; a.dw = L.dw; a.dcap = L.ND;
 
   hipError_t e = launch_zero_u32(base, L.total_words, st);

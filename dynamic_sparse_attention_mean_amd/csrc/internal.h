@@ -73,6 +73,8 @@ struct AttnArgs {
   uint32_t* dbits;                   // bit e set iff a selected diagonal lies in [32e - 31, 32e + 31]
   int32_t* dlist; int32_t* dcount; int32_t* dle;   // those e ascending, their number, #{e' <= e}
   int sw, vw, dw, dcap;              // words per head of each bitmap; dlist capacity
+  int32_t* win;                      // [B*H][2]: window length and sink of a head whose sets are
+                                     // cols = [0, sink), diags = [0, window) (else window = -1)
   // Block sets
   const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
   // Token sets
