@@ -304,7 +304,6 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   if (use[DSA_PATTERN_VS]) {
     if (!vs || !vs->cols || !vs->cols_count || !vs->diags || !vs->diags_count || vs->cols_cap < 0 || vs->diags_cap < 0)
       return fail(DSA_ERR_INVALID_ARG, "VS heads need a VS index set");
-    if (shape->q_offset % 64 != 0) return fail(DSA_ERR_UNSUPPORTED, "VS heads need q_offset %% 64 == 0");
   }
   if (use[DSA_PATTERN_BLOCK]) {
     if (!blk || !blk->idx || !blk->count || blk->cap < 1) return fail(DSA_ERR_INVALID_ARG, "block heads need a block index set");

@@ -1,7 +1,7 @@
 """GPU parity of sparse attention on shapes the five workloads do not reach:
 batch > 1, GQA ratios 1 and 8, Vertical-Slash heads in a chunk that starts
-after key 0 (q_offset > 0), and one call that mixes token-list heads with
-Vertical-Slash, block and dense heads.  Every head is fed the oracle's own
+after key 0 (q_offset > 0, also not tile-aligned), and one call that mixes
+token-list heads with Vertical-Slash, block and dense heads.  Every head is fed the oracle's own
 index set and compared with the fp64 oracle on every row."""
 import numpy as np
 import pytest
@@ -73,6 +73,14 @@ def test_vertical_slash_chunk_after_key0():
     rows' absolute positions."""
     heads = [vs(64, 50, 90), ashape(32, 200), dense(), vs(33, 10, 300)]
     run_and_check(workload(50, 1, 4, 2, 1280, heads, Nq=320), "chunk")
+
+
+def test_chunk_offset_not_tile_aligned():
+    """A 333-row chunk at the end of 1000 keys (q_offset = 667, a multiple of
+    neither 32 nor 64): Vertical-Slash sub-blocks start mid-tile and the
+    window heads' first tiles are partial."""
+    heads = [vs(64, 50, 90), ashape(32, 200), dense(), vs(33, 10, 300)]
+    run_and_check(workload(51, 1, 4, 2, 1000, heads, Nq=333), "unaligned chunk")
 
 
 def test_token_heads_mixed_with_other_kinds():
