@@ -203,6 +203,25 @@ def time_steps(fns, steps, warmup, stream):
     return total, phases, wall
 
 
+def time_cold(fns, reps, stream, flush_bytes=512 << 20):
+    """Cold-cache steps: before each, a write of `flush_bytes` of scratch evicts the inputs from L2
+    and the 256 MB Infinity Cache; HIP events bracket only the step's phases."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=torch.device("cuda", 0))
+    tot, ph = [], []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        tot.append(ev[0].elapsed_time(ev[-1]))
+        ph.append([ev[j].elapsed_time(ev[j + 1]) for j in range(len(fns))])
+    del scratch
+    return float(np.mean(tot)), [float(np.mean([x[j] for x in ph])) for j in range(len(fns))]
+
+
 def attn_src_digest():
     h = hashlib.sha256()
     for p in ATTN_SRCS:
@@ -280,6 +299,8 @@ def main():
                                                lse=lse, ws=aws)
         log(f"[bench] timing {args.steps} steps")
         ms_step, (ms_index, ms_attn), wall = time_steps([build, attn], args.steps, args.warmup, stream)
+        cold, (cold_i, cold_a) = time_cold([build, attn], 3, stream)
+        extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
         n_sel = int(tok.count.sum().item()) * H
         f_sel = 4 * d * n_sel
         hsel = qi.shape[1] if route == 0 else route
@@ -292,9 +313,10 @@ def main():
         layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
         torch.cuda.synchronize()
         log(f"[bench] timing {args.steps} steps")
-        ms_step, (ms_index, ms_attn), wall = time_steps([lambda: layer.build_indices(q, k),
-                                                         lambda: layer.attention(q, k, v)],
-                                                        args.steps, args.warmup, stream)
+        phases = [lambda: layer.build_indices(q, k), lambda: layer.attention(q, k, v)]
+        ms_step, (ms_index, ms_attn), wall = time_steps(phases, args.steps, args.warmup, stream)
+        cold, (cold_i, cold_a) = time_cold(phases, 3, stream)
+        extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
         f_sel = 4 * d * selected_count_layer(layer, w)
         if args.workload.startswith("thresh"):
             # the dense causal comparison on the same inputs (informative)
