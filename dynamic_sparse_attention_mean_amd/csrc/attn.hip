@@ -169,6 +169,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 // 16 bytes per lane straight from global memory into LDS; lane l of the wave
 // lands at LDS byte address lds_addr + 16 l (lds_addr is wave-uniform).
@@ -381,6 +382,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
   const int v_half = (si & 1) * 8;
   // LDS byte address of the arena (64-key ring: stage s, K (0) or V (1) at + (2 s + kv) * 16 KB)
   const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)&s_lds[0]);
+  // This lane's LDS addresses of its K fragments (row qn of a 32-key block, chunk 2 ks + hh) and V
+  // fragments (row v_row0, the chunk of d block db), arena base included.  The swizzle makes them
+  // lane-dependent; every other part of an address (ring stage, key half, 16-key step) is then an
+  // immediate offset of the read.
+  uint32_t kaddr[8], vaddr[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kaddr[ks] = ring + qn * 256 + swz_k(qn, 2 * ks + hh) * 16;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    vaddr[db] = ring + v_row0 * 256 + swz_v(v_row0, 4 * db + 2 * (G & 1) + ((si & 3) >> 1)) * 16 + v_half;
 
   for (int qi = 0; qi < sc.nq; ++qi) {
     const int g = (myq + qi) % sc.nq;
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       // One 32x32 sub-block: S^T = K Q^T over the 32 keys whose swizzled K rows
       // start at kbase, online softmax under the mask M (bit c <-> key c of this
       // lane's row), O^T += V^T P^T with the V rows at vbase.
-      auto sub32 = [&](const char* kbase, const lds_char_t* vbase, uint32_t M) {
+      auto sub32 = [&](uint32_t kofs, uint32_t vofs, uint32_t M) {
         if (!row_ok) M = 0u;
         if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) return;
         const bool masked = __builtin_amdgcn_ballot_w64(M != ~0u) != 0;
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
         u32x4 kf[8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(kbase + qn * 256 + swz_k(qn, 2 * ks + hh) * 16);
+        for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const lds_u32x4_t*)(uintptr_t)(kaddr[ks] + kofs);
         DSA_PRIO_HI();
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
@@ -509,16 +520,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
           const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
-          const int rowa = 16 * s2 + v_row0;
-          const int rowb = rowa + 8;
+          // rows 16 s2 + v_row0 (a) and + 8 (b): the same swizzle as row v_row0
           short4_t ya[4], yb[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const int cch = 4 * db + 2 * (G & 1) + ((si & 3) >> 1);
-            ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4_t*)(vbase + rowa * 256 + swz_v(rowa, cch) * 16 + v_half));
+            ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)(vaddr[db] + vofs + 16 * s2 * 256));
             yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4_t*)(vbase + rowb * 256 + swz_v(rowb, cch) * 16 + v_half));
+                (lds_short4_t*)(uintptr_t)(vaddr[db] + vofs + (16 * s2 + 8) * 256));
           }
           DSA_PRIO_HI();
 #pragma unroll
@@ -635,7 +643,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               }
               if (ec == 0) M &= causal_mask32(qn);
               const int sl = mod5(u);
-              sub32(s_lds + sl * SLOT, (const lds_char_t*)(s_lds + sl * SLOT + 8192), M);
+              sub32(sl * SLOT, sl * SLOT + 8192, M);
             }
             if (--k < 0) break;
             ep = ec;
@@ -744,8 +752,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             issue_tile<false>(kbp, a.Nk, nxt, s_cols, ring + (stage ^ 1) * 2 * TK * 256, w, l, off_k);
             issue_tile<true>(vbp, a.Nk, nxt, s_cols, ring + ((stage ^ 1) * 2 + 1) * TK * 256, w, l, off_v);
           }
-          const char* sk = s_lds + stage * 2 * TK * 256;
-          const lds_char_t* sv = (const lds_char_t*)(s_lds + (stage * 2 + 1) * TK * 256);
 
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
@@ -781,7 +787,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const bool ex = (s_cov[base + (l & 31)] >> w) & 1u;
               M &= ~(uint32_t)__builtin_amdgcn_ballot_w64(ex);
             }
-            sub32(sk + 32 * kb * 256, sv + 32 * kb * 256, M);
+            sub32(stage * 2 * TK * 256 + 32 * kb * 256, (stage * 2 + 1) * TK * 256 + 32 * kb * 256, M);
           }
           cur = nxt;
           have = have_n;
