@@ -600,23 +600,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
         };
         if (k >= 0) {
-          int ec = ldc(dl, k);
-          for (int u = -ec; u <= 3 - ec; ++u) issue_block(u);
-          int ep = -1;
           const bool wave_on = R0w <= it.last_pos;
+          // Scalar words a step needs: the diagonal bitmap words of its offset
+          // window and this wave's column words.  They are loaded one step
+          // ahead, with the list entry two steps ahead, so that their latency
+          // hides behind a step's arithmetic.
+          struct StepWords {
+            uint32_t d0, d1, c0, c1;
+          };
+          auto load_words = [&](int e) {
+            StepWords sw = {0u, 0u, 0u, 0u};
+            const int k0 = it.P0 + 32 * (w - e);
+            if (e >= 0 && wave_on && k0 + 31 >= 0) {
+              sw.d0 = ldc(sbits, e + 1);
+              sw.d1 = ldc(sbits, e + 2);
+              sw.c0 = ldc(vbits, max(k0, 0) >> 5);
+              sw.c1 = k0 >= 0 ? ldc(vbits, (k0 >> 5) + 1) : 0u;
+            }
+            return sw;
+          };
+          int ec = ldc(dl, k);
+          int en = k >= 1 ? ldc(dl, k - 1) : -1;
+          for (int u = -ec; u <= 3 - ec; ++u) issue_block(u);
+          StepWords wc = load_words(ec);
+          int ep = -1;
           while (true) {
-            const int en = k > 0 ? ldc(dl, k - 1) : -1;
             const int u = w - ec;
             const int k0 = it.P0 + 32 * u;
             const bool active = wave_on && k0 + 31 >= 0;
-            // diagonal words (offsets [32 ec - 32, 32 ec + 31]) and this block's column words
-            uint32_t D0 = 0u, D1 = 0u, C0 = 0u, C1 = 0u;
-            if (active) {
-              D0 = ldc(sbits, ec + 1);
-              D1 = ldc(sbits, ec + 2);
-              C0 = ldc(vbits, max(k0, 0) >> 5);
-              C1 = k0 >= 0 ? ldc(vbits, (k0 >> 5) + 1) : 0u;
-            }
             wait_vm();
             __syncthreads();                     // this step's blocks landed; the previous step is done
             if (ep >= 0) {
@@ -632,14 +643,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
                 if (mod5(v - (4 - ec)) == 0) issue_block(v);
             }
+            // the next step's words and the list entry after it
+            const StepWords wn = load_words(en);
+            const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
             if (active) {
               // lane row r sees offsets 32 ec + r - c for keys c = 0..31
-              const uint64_t dwin = ((uint64_t)D1 << 32) | D0;
+              const uint64_t dwin = ((uint64_t)wc.d1 << 32) | wc.d0;
               uint32_t M = __builtin_bitreverse32((uint32_t)(dwin >> (1 + qn)));
               if (k0 >= 0) {
-                M |= (uint32_t)((((uint64_t)C1 << 32) | C0) >> (k0 & 31));
+                M |= (uint32_t)((((uint64_t)wc.c1 << 32) | wc.c0) >> (k0 & 31));
               } else {
-                M = (M | (C0 << (-k0))) & (~0u << (-k0));
+                M = (M | (wc.c0 << (-k0))) & (~0u << (-k0));
               }
               if (ec == 0) M &= causal_mask32(qn);
               const int sl = mod5(u);
@@ -648,6 +662,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             if (--k < 0) break;
             ep = ec;
             ec = en;
+            en = enn;
+            wc = wn;
           }
         }
         __syncthreads();                         // the slots are free for the gather phase
