@@ -265,6 +265,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed128k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (profiling runs: every launch is then a warm one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -299,8 +301,9 @@ def main():
                                                lse=lse, ws=aws)
         log(f"[bench] timing {args.steps} steps")
         ms_step, (ms_index, ms_attn), wall = time_steps([build, attn], args.steps, args.warmup, stream)
-        cold, (cold_i, cold_a) = time_cold([build, attn], 3, stream)
-        extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
+        if not args.no_cold:
+            cold, (cold_i, cold_a) = time_cold([build, attn], 3, stream)
+            extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
         n_sel = int(tok.count.sum().item()) * H
         f_sel = 4 * d * n_sel
         hsel = qi.shape[1] if route == 0 else route
@@ -315,8 +318,9 @@ def main():
         log(f"[bench] timing {args.steps} steps")
         phases = [lambda: layer.build_indices(q, k), lambda: layer.attention(q, k, v)]
         ms_step, (ms_index, ms_attn), wall = time_steps(phases, args.steps, args.warmup, stream)
-        cold, (cold_i, cold_a) = time_cold(phases, 3, stream)
-        extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
+        if not args.no_cold:
+            cold, (cold_i, cold_a) = time_cold(phases, 3, stream)
+            extra.update(ms_step_cold=round(cold, 4), ms_index_cold=round(cold_i, 4), ms_attn_cold=round(cold_a, 4))
         f_sel = 4 * d * selected_count_layer(layer, w)
         if args.workload.startswith("thresh"):
             # the dense causal comparison on the same inputs (informative)
