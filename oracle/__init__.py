@@ -21,8 +21,9 @@ per function, each citing the passage it follows.  Pages cited:
 Parity status: every function is pinned by a test in ``tests/test_oracle.py``
 against brute force, a closed form or a library routine, except the choices
 the pages leave open (router aggregation, forced blocks with the threshold
-rule, indexer key sharing); those are "parity unpinned" beyond brute force of
-the chosen definition, as stated in their docstrings.
+rule, indexer key sharing, the two stages of the hierarchical indexer); those
+are "parity unpinned" beyond brute force of the chosen definition, as stated
+in their docstrings.
 """
 from .bf16 import round_bf16, to_f64
 from .rules import (
@@ -32,7 +33,7 @@ from .rules import (
     row_set_vs, row_set_block, row_set_dense,
 )
 from .attention import masked_attention, attention_rows
-from .indexer import indexer_scores, router_heads, token_topk, indexer_row
+from .indexer import indexer_scores, router_heads, token_topk, indexer_row, hierarchical_tokens
 from .work import selected_count_vs, selected_count_block, selected_count_dense
 
 __all__ = [
@@ -42,6 +43,6 @@ __all__ = [
     "mask_dense", "mask_vs", "mask_block", "mask_tokens",
     "row_set_vs", "row_set_block", "row_set_dense",
     "masked_attention", "attention_rows",
-    "indexer_scores", "router_heads", "token_topk", "indexer_row",
+    "indexer_scores", "router_heads", "token_topk", "indexer_row", "hierarchical_tokens",
     "selected_count_vs", "selected_count_block", "selected_count_dense",
 ]

@@ -64,3 +64,35 @@ def router_heads(q_idx, k_idx, w, q_offset, route_heads=8, block=64, rows=None):
 def token_topk(scores_row, p, k):
     """Top-k keys of one query among j <= p, ascending."""
     return topk_rule(scores_row, np.arange(p + 1), k)
+
+
+def hierarchical_tokens(q_idx, k_idx, w, q_offset, route_heads, cand, k, block=64, rows=None):
+    """Two-stage token selection of MISA's hierarchical variant, per query row.
+
+    [MISA] section "how MISA works", the hierarchical option: first the
+    router's few heads score the keys and keep a larger candidate list; then
+    all of the indexer heads score only those candidates, and the best of
+    them are kept.  Readings (the explainer gives no sizes or formulas):
+      * stage 1: H(i) = router_heads(...); candidates C(i) = top-`cand` keys
+        j <= p_i by the routed score (ties to the lower index);
+      * stage 2: the dense score (all heads) of each candidate; the result is
+        the top-`k` of C(i) by that score (ties to the lower index), ascending,
+        min(k, |C(i)|) keys.
+    Parity unpinned beyond brute force and the special cases that reduce it
+    to the dense or the routed indexer (cand >= p_i + 1; route_heads = all
+    heads; cand = k).
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    rows = range(q_idx.shape[0]) if rows is None else rows
+    rows = list(rows)
+    heads = router_heads(q_idx, k_idx, w, q_offset, route_heads, block, rows=rows)
+    out = []
+    for n, i in enumerate(rows):
+        p = i + q_offset
+        routed = indexer_row(q_idx[i], k_idx, w[i], p, heads[n])
+        c_set = topk_rule(routed, np.arange(p + 1), cand)
+        full = np.full(p + 1, -np.inf)
+        full[c_set] = indexer_row(q_idx[i], np.asarray(k_idx)[c_set], w[i], len(c_set) - 1)
+        out.append(topk_rule(full, c_set, k))
+    return out

@@ -421,6 +421,54 @@ def test_router_brute_force():
         assert route[i].tolist() == ref
 
 
+def test_hierarchical_brute_force():
+    """Both stages written out with plain loops and sorts on a tiny chunk."""
+    nq, nk, Hi, di, blk, qo = 4, 48, 6, 8, 8, 40
+    q = bf16_array((nq, Hi, di))
+    k = bf16_array((nk, di))
+    w = RNG.random((nq, Hi))
+    r, cand, kk = 2, 12, 5
+    got = O.hierarchical_tokens(q, k, w, qo, r, cand, kk, block=blk)
+    for i in range(nq):
+        p = i + qo
+        nc = (p + 1) // blk
+        kbar = [O.round_bf16(k[J * blk:(J + 1) * blk].sum(0) / blk) for J in range(nc)]
+        rr = [w[i, h] * max(0.0, max(float(q[i, h] @ kb) for kb in kbar)) for h in range(Hi)]
+        heads = sorted(range(Hi), key=lambda h: (-rr[h], h))[:r]
+        routed = [sum(w[i, h] * max(0.0, float(q[i, h] @ k[j])) for h in heads) for j in range(p + 1)]
+        c_set = sorted(range(p + 1), key=lambda j: (-routed[j], j))[:cand]
+        full = {j: sum(w[i, h] * max(0.0, float(q[i, h] @ k[j])) for h in range(Hi)) for j in c_set}
+        ref = sorted(sorted(c_set, key=lambda j: (-full[j], j))[:kk])
+        assert got[i].tolist() == ref
+
+
+def test_hierarchical_special_cases():
+    nq, nk, Hi, di, blk, qo = 5, 64, 6, 8, 8, 59
+    q = bf16_array((nq, Hi, di))
+    k = bf16_array((nk, di))
+    w = RNG.random((nq, Hi))
+    dense = O.indexer_scores(q, k, w, qo)
+    for kk in (1, 7, 30):
+        dense_sets = [O.token_topk(dense[i], i + qo, kk) for i in range(nq)]
+        # every causal key a candidate: the dense indexer
+        for a, b in zip(O.hierarchical_tokens(q, k, w, qo, 2, nk, kk, block=blk), dense_sets):
+            assert np.array_equal(a, b)
+        # every head routed: stage 1 ranks by the dense score, so any cand >= k gives the dense top-k
+        for a, b in zip(O.hierarchical_tokens(q, k, w, qo, Hi, kk + 3, kk, block=blk), dense_sets):
+            assert np.array_equal(a, b)
+        # cand = k: the routed indexer's own top-k
+        route = O.router_heads(q, k, w, qo, 2, blk)
+        routed = O.indexer_scores(q, k, w, qo, heads=route)
+        for i, a in enumerate(O.hierarchical_tokens(q, k, w, qo, 2, kk, kk, block=blk)):
+            assert np.array_equal(a, O.token_topk(routed[i], i + qo, kk))
+    # the result is a subset of the candidates, of size min(k, cand, p + 1)
+    route = O.router_heads(q, k, w, qo, 2, blk)
+    routed = O.indexer_scores(q, k, w, qo, heads=route)
+    for i, a in enumerate(O.hierarchical_tokens(q, k, w, qo, 2, 20, 9, block=blk)):
+        c_set = O.token_topk(routed[i], i + qo, 20)
+        assert set(a.tolist()) <= set(c_set.tolist()) and len(a) == 9
+
+
 # ---------------------------------------------------------------------------
 # Hand-written closed-form fixtures
 # ---------------------------------------------------------------------------
