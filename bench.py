@@ -53,6 +53,9 @@ WORKLOADS = {
                     "(16 heads)", lambda: synth.config(5)),
     "indexer128k-routed": ("indexer top-2048 over N=131072, 8 of 64 heads routed per query + token attention "
                            "(16 heads)", lambda: synth.config(5, route_heads=8)),
+    "indexer128k-hier": ("hierarchical indexer top-2048 over N=131072: 8 of 64 heads routed per query pick 8192 "
+                         "candidates, all 64 heads rescore them + token attention (16 heads)",
+                         lambda: synth.config(5, route_heads=8, cand=8192)),
 }
 
 
@@ -156,7 +159,7 @@ def cpu_baseline_indexer(w, sample_queries=32, seed=0):
     from oracle.bf16 import to_f64
     B, H, Hkv, Nq, Nk, d = w.shape
     qi, ki, wt = w.extra["q_idx"], w.extra["k_idx"], w.extra["w"]
-    topk, route = w.extra["topk"], w.extra["route_heads"]
+    topk, route, cand = w.extra["topk"], w.extra["route_heads"], w.extra.get("cand", 0)
     rows = np.sort(np.random.default_rng(seed).choice(Nq, sample_queries, replace=False))
     kf = to_f64(ki)
     t_index = t_attn = 0.0
@@ -164,6 +167,11 @@ def cpu_baseline_indexer(w, sample_queries=32, seed=0):
     for i in rows:
         p = int(i) + w.q_offset
         t0 = time.perf_counter()
+        if cand:
+            sets.append(O.hierarchical_tokens(to_f64(qi[i:i + 1]), kf, wt[i:i + 1].double().numpy(), p, route, cand,
+                                              topk)[0])
+            t_index += time.perf_counter() - t0
+            continue
         heads = None
         if route:
             heads = O.router_heads(to_f64(qi[i:i + 1]), kf, wt[i:i + 1].double().numpy(), p, route_heads=route)[0]
@@ -179,7 +187,8 @@ def cpu_baseline_indexer(w, sample_queries=32, seed=0):
         t_attn += time.perf_counter() - t0
     scale = Nq / sample_queries
     return dict(t_index=t_index * scale, t_attn_layer=t_attn * scale, t_attn_sample=t_attn,
-                threads=_oracle_threads(), sample=f"router + indexer scores + top-{topk} and attention of all {H} "
+                threads=_oracle_threads(), sample=f"router + indexer scores + top-{topk}"
+                + (f" of {cand} rescored candidates" if cand else "") + f" and attention of all {H} "
                 f"heads on {sample_queries} random queries of the chunk, scaled to {Nq} queries")
 
 
@@ -288,15 +297,22 @@ def main():
 
     if args.workload.startswith("indexer"):
         qi, ki, wt = w.extra["q_idx"].to(dev), w.extra["k_idx"].to(dev), w.extra["w"].to(dev)
-        topk, route = w.extra["topk"], w.extra["route_heads"]
+        topk, route, cand = w.extra["topk"], w.extra["route_heads"], w.extra.get("cand", 0)
         tok = dsa.TokenIndex.empty(1, Nq, topk, dev)
         shape = dsa.Shape(1, 1, 1, Nq, Nk, 128, Nk - Nq)
-        ws = torch.empty(dsa.workspace_size(dsa.OP_TOKENS, shape, [qi.shape[1], route, topk]), dtype=torch.uint8,
-                         device=dev)
+        if cand:
+            ws = torch.empty(dsa.workspace_size(dsa.OP_TOKENS_HIER, shape, [qi.shape[1], route, cand, topk]),
+                             dtype=torch.uint8, device=dev)
+        else:
+            ws = torch.empty(dsa.workspace_size(dsa.OP_TOKENS, shape, [qi.shape[1], route, topk]), dtype=torch.uint8,
+                             device=dev)
         o = torch.empty(1, H, Nq, d, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(1, H, Nq, dtype=torch.float32, device=dev)
         aws = torch.empty(dsa.workspace_size(dsa.OP_ATTN, dsa.make_shape(q, k)), dtype=torch.uint8, device=dev)
-        build = lambda: dsa.build_index_tokens(qi, ki, wt, topk, tok, route_heads=route, ws=ws)
+        if cand:
+            build = lambda: dsa.build_index_tokens_hier(qi, ki, wt, cand, topk, tok, route_heads=route, ws=ws)
+        else:
+            build = lambda: dsa.build_index_tokens(qi, ki, wt, topk, tok, route_heads=route, ws=ws)
         attn = lambda: dsa.sparse_prefill_attn(q, k, v, [dsa.TOKEN] * H, tok=tok, out_dtype=dsa.OUT_BF16, o=o,
                                                lse=lse, ws=aws)
         log(f"[bench] timing {args.steps} steps")
@@ -309,6 +325,9 @@ def main():
         hsel = qi.shape[1] if route == 0 else route
         pos = np.arange(Nq, dtype=np.float64) + (Nk - Nq)
         extra["indexer_flop"] = float(2 * 128 * hsel * (pos + 1).sum())
+        if cand:
+            # the rescoring of the candidates by every head
+            extra["indexer_flop"] += float(2 * 128 * qi.shape[1] * np.minimum(pos + 1, cand).sum())
         extra["indexer_tflops"] = round(extra["indexer_flop"] / (ms_index * 1e-3) / 1e12, 2)
         extra["gather_bytes"] = n_sel * 2 * d * 2
         extra["token_attn_gbs"] = round(extra["gather_bytes"] / (ms_attn * 1e-3) / 1e9, 1)
@@ -358,7 +377,10 @@ def main():
     if args.workload.startswith("indexer"):
         rec["roofline"] = {"bound": "mfma", "achieved": extra["indexer_tflops"], "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(extra["indexer_tflops"] / PEAK_BF16_TFLOPS, 4),
-                           "traffic": None, "kernel": "qk_heads_kernel + token_select_kernel (build_index_tokens)"}
+                           "traffic": None,
+                           "kernel": ("qk_heads_kernel + token_select_kernel + cand_score_kernel + cand_select_kernel "
+                                      "(build_index_tokens_hier)") if w.extra.get("cand", 0) else
+                                     "qk_heads_kernel + token_select_kernel (build_index_tokens)"}
     else:
         rec["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),

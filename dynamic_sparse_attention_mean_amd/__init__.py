@@ -23,11 +23,11 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 DENSE, VS, BLOCK, TOKEN = 0, 1, 2, 3
 TOPK, THRESHOLD = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
-OP_VS, OP_BLOCK, OP_TOKENS, OP_ATTN = 1, 2, 3, 4
+OP_VS, OP_BLOCK, OP_TOKENS, OP_ATTN, OP_TOKENS_HIER = 1, 2, 3, 4, 5
 
 EXPORTS = (
     "dsa_status_string", "dsa_last_error", "dsa_workspace_size", "build_index_ashape",
-    "build_index_vs", "build_index_block", "build_index_tokens", "sparse_prefill_attn",
+    "build_index_vs", "build_index_block", "build_index_tokens", "build_index_tokens_hier", "sparse_prefill_attn",
 )
 
 
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
                                         _BlockIndexC, P, P, P, P, SZ, P]
         L.build_index_tokens.restype = I32
         L.build_index_tokens.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, _TokenIndexC, P, P, SZ, P]
+        L.build_index_tokens_hier.restype = I32
+        L.build_index_tokens_hier.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, _TokenIndexC,
+                                              ctypes.POINTER(_TokenIndexC), P, P, SZ, P]
         L.sparse_prefill_attn.restype = I32
         L.sparse_prefill_attn.argtypes = [ctypes.POINTER(Shape), P, P, P, P, ctypes.POINTER(_VsIndexC),
                                           ctypes.POINTER(_BlockIndexC), ctypes.POINTER(_TokenIndexC), I32, P, P, P,
@@ -239,6 +242,24 @@ def build_index_tokens(q_idx, k_idx, w, topk, out: TokenIndex, route_heads=0, ro
     _check(lib().build_index_tokens(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads, topk,
                                     out.c(), _ptr(route), _ptr(ws), ws.numel(), _stream(q_idx.device)),
            "build_index_tokens")
+    return out
+
+
+def build_index_tokens_hier(q_idx, k_idx, w, cand, topk, out: TokenIndex, route_heads=8, cands=None, route=None,
+                            ws=None):
+    """Hierarchical indexer: routed top-`cand` candidates, rescored by every head, top-`topk` of them."""
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, q_idx.device)
+    _need(w, "w", torch.float32, q_idx.device)
+    Nq, Hi, di = q_idx.shape
+    Nk = k_idx.shape[0]
+    shape = Shape(1, 1, 1, Nq, Nk, di, Nk - Nq)
+    ws = _workspace(OP_TOKENS_HIER, shape, [Hi, route_heads, cand, topk], q_idx.device, ws)
+    cc = cands.c() if cands is not None else None
+    _check(lib().build_index_tokens_hier(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads, cand,
+                                         topk, out.c(), ctypes.byref(cc) if cc is not None else None, _ptr(route),
+                                         _ptr(ws), ws.numel(), _stream(q_idx.device)),
+           "build_index_tokens_hier")
     return out
 
 

@@ -129,7 +129,13 @@ dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t*
     case DSA_OP_TOKENS:
       if (!need(3) || params[0] < 1 || params[1] < 0 || params[1] > params[0] || params[2] < 1)
         return fail(DSA_ERR_INVALID_ARG, "TOKENS params");
-      *bytes = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, params[0], params[1])) + 256;
+      *bytes = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, params[0], params[1], 0)) + 256;
+      return DSA_OK;
+    case DSA_OP_TOKENS_HIER:
+      if (!need(4) || params[0] < 1 || params[1] < 1 || params[1] > params[0] || params[3] < 1 ||
+          params[2] < params[3] || params[2] > kMaxCandidates)
+        return fail(DSA_ERR_INVALID_ARG, "TOKENS_HIER params");
+      *bytes = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, params[0], params[1], params[2])) + 256;
       return DSA_OK;
     case DSA_OP_ATTN:
       *bytes = ws_attn(shape);
@@ -270,7 +276,43 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
   if (!out.idx || !out.count) return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
   if (out.cap < std::min(topk, shape->kv_len)) return fail(DSA_ERR_INVALID_ARG, "out.cap < topk");
-  const size_t need = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, n_idx_heads, route_heads)) + 256;
+  const size_t need = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, n_idx_heads, route_heads, 0)) + 256;
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  IndexerArgs a;
+  a.cand = 0;
+  a.cand_idx = nullptr; a.cand_count = nullptr; a.cand_cap = 0;
+  a.q_idx = (const uint16_t*)q_idx;
+  a.k_idx = (const uint16_t*)k_idx;
+  a.w = w;
+  a.Nq = shape->q_len; a.Nk = shape->kv_len; a.Hi = n_idx_heads; a.q_offset = shape->q_offset;
+  a.route_heads = route_heads; a.topk = topk;
+  a.tok = out.idx; a.tok_count = out.count; a.tok_cap = out.cap;
+  a.route = route;
+  return hip_status(launch_indexer(a, ws, (hipStream_t)stream), "build_index_tokens");
+}
+
+dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, const void* k_idx, const float* w,
+                                   int32_t n_idx_heads, int32_t route_heads, int32_t cand, int32_t topk,
+                                   dsa_token_index out, const dsa_token_index* cands, int32_t* route, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  g_err.clear();
+  dsa_status st = check_shape(shape);
+  if (st) return st;
+  if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx or w is null");
+  if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
+  if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
+  if (route_heads < 1 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
+  if (route_heads > 8) return fail(DSA_ERR_UNSUPPORTED, "route_heads > 8");
+  if (shape->kv_len > (1 << 27)) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes kv_len <= 2^27");
+  if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
+  if (topk > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "topk > %d", kMaxTokensPerQuery);
+  if (cand < topk || cand > kMaxCandidates) return fail(DSA_ERR_INVALID_ARG, "cand must be in [topk, %d]", kMaxCandidates);
+  if (!out.idx || !out.count) return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
+  if (out.cap < std::min(topk, shape->kv_len)) return fail(DSA_ERR_INVALID_ARG, "out.cap < topk");
+  if (cands && (!cands->idx || !cands->count || cands->cap < cand))
+    return fail(DSA_ERR_INVALID_ARG, "cands: null pointers or cap < cand");
+  const size_t need =
+      align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, n_idx_heads, route_heads, cand)) + 256;
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   IndexerArgs a;
   a.q_idx = (const uint16_t*)q_idx;
@@ -280,7 +322,11 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   a.route_heads = route_heads; a.topk = topk;
   a.tok = out.idx; a.tok_count = out.count; a.tok_cap = out.cap;
   a.route = route;
-  return hip_status(launch_indexer(a, ws, (hipStream_t)stream), "build_index_tokens");
+  a.cand = cand;
+  a.cand_idx = cands ? cands->idx : nullptr;
+  a.cand_count = cands ? cands->count : nullptr;
+  a.cand_cap = cands ? cands->cap : cand;
+  return hip_status(launch_indexer(a, ws, (hipStream_t)stream), "build_index_tokens_hier");
 }
 
 dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,

@@ -20,6 +20,12 @@
 //     in a lane, so the head sum is 16 in-lane FMAs plus one lane swap.
 //   router_select_kernel: top-r heads per query (rank counting over 64 values).
 //   token_select_kernel: radix top-k per query row (select.h).
+//   Hierarchical option (MISA section on how it works, the two-stage variant):
+//     the routed scores pick `cand` candidates per query (token_select_kernel),
+//     cand_score_kernel rescores them with every head (the query's 64 head rows
+//     as the MFMA A operand, the gathered candidate keys as B, read straight
+//     from global memory: each query has its own keys, so there is nothing to
+//     share through LDS), and cand_select_kernel keeps the top-k of them.
 //   token_attn_kernel: per (query, head) softmax over the gathered token list on
 //     VALU; the grid is head-major so a head's K/V stays in the Infinity Cache.
 #include "common.h"
@@ -280,6 +286,93 @@ __global__ __launch_bounds__(TS_THREADS) void token_select_kernel(const float* s
   if (threadIdx.x == 0) cnt[q] = m;
 }
 
+// ---------------------------------------------------------------- hierarchical option
+constexpr int CS_WAVES = 4;       // queries (waves) per workgroup
+
+// score[q, c] = sum_h w[q, h] max(0, q_idx[q, h] . k_idx[cand[q, c]]) for c < ccount[q].
+// One wave per query: rows 32 hb + m of the A operand are heads, columns the
+// 32 candidates of a block; the next block's keys are loaded while this one's
+// MFMAs run.
+__global__ __launch_bounds__(CS_WAVES * 64) void cand_score_kernel(const uint16_t* __restrict__ q_idx,
+                                                                   const uint16_t* __restrict__ k_idx,
+                                                                   const float* __restrict__ w,
+                                                                   const int32_t* __restrict__ cand,
+                                                                   const int32_t* __restrict__ ccount, int Nq, int Hi,
+                                                                   int ccap, float* __restrict__ out) {
+  const int wv_ = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = blockIdx.x * CS_WAVES + wv_;
+  if (q >= Nq) return;
+  const int l = threadIdx.x & 63, qn = l & 31, hh = l >> 5;
+  bf16x8 af[2][8];
+  float wv[2][16];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = 32 * hb + qn;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (head < Hi) x = *(const u32x4*)(q_idx + ((size_t)q * Hi + head) * 128 + 16 * ks + 8 * hh);
+      af[hb][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h2 = 32 * hb + 8 * (v >> 2) + 4 * hh + (v & 3);
+      wv[hb][v] = h2 < Hi ? w[(size_t)q * Hi + h2] : 0.f;
+    }
+  }
+  const int n = __builtin_amdgcn_readfirstlane(ccount[q]);
+  const int32_t* cq = cand + (size_t)q * ccap;
+  float* oq = out + (size_t)q * ccap;
+  const int nb = (n + 31) / 32;
+  // this lane's key row of block b: candidate 32 b + qn (the first one past the end)
+  auto load = [&](int b, u32x4 (&kf)[8]) {
+    const int c = 32 * b + qn;
+    const int key = cq[c < n ? c : 0];
+    const uint16_t* row = k_idx + (size_t)key * 128 + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(row + 16 * ks);
+  };
+  u32x4 kc[8], kn[8];
+  if (nb > 0) load(0, kc);
+  for (int b = 0; b < nb; ++b) {
+    if (b + 1 < nb) load(b + 1, kn);
+    f32x16 c[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c[hb][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        c[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[hb][ks], __builtin_bit_cast(bf16x8, kc[ks]), c[hb], 0, 0, 0);
+    }
+    float sacc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc = __builtin_fmaf(wv[hb][v], fmaxf(c[hb][v], 0.f), sacc);
+    const float tot = sacc + __shfl_xor(sacc, 32, 64);
+    const int col = 32 * b + qn;
+    if (hh == 0 && col < n) oq[col] = tot;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kc[ks] = kn[ks];
+  }
+}
+
+// Top-k of a query's rescored candidates (ties to the lower position, which is
+// the lower key: candidate lists ascend), mapped back to key indices.
+__global__ __launch_bounds__(TS_THREADS) void cand_select_kernel(const float* scores, const int32_t* cand,
+                                                                 const int32_t* ccount, int ccap, int k, int32_t* tok,
+                                                                 int32_t* cnt, int cap) {
+  __shared__ Select3Smem<TS_THREADS> sm;
+  __shared__ int32_t pos[kMaxTokensPerQuery];
+  const int q = blockIdx.x;
+  const int n = ccount[q];
+  const int m = select_topk_3pass<TS_THREADS>(scores + (size_t)q * ccap, n, min(k, kMaxTokensPerQuery), pos, sm);
+  __syncthreads();
+  for (int r = threadIdx.x; r < m; r += TS_THREADS) tok[(size_t)q * cap + r] = cand[(size_t)q * ccap + pos[r]];
+  if (threadIdx.x == 0) cnt[q] = m;
+}
+
 // ---------------------------------------------------------------- token attention
 constexpr int TA_THREADS = 256;
 constexpr int TA_MAXTOK = 4096;
@@ -419,9 +512,9 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
 }
 
 struct IdxLayout {
-  size_t off_scores, off_kbar, off_r, off_route, total;
+  size_t off_scores, off_kbar, off_r, off_route, off_cand, off_ccnt, off_resc, total;
 };
-IdxLayout idx_layout(int Nq, int Nk, int Hi, int R) {
+IdxLayout idx_layout(int Nq, int Nk, int Hi, int R, int cand) {
   IdxLayout L;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 0;
@@ -429,19 +522,22 @@ IdxLayout idx_layout(int Nq, int Nk, int Hi, int R) {
   L.off_kbar = off; off = al(off + (size_t)((Nk + 63) / 64) * 128 * 2);
   L.off_r = off; off = al(off + (size_t)Nq * Hi * 4);
   L.off_route = off; off = al(off + (size_t)Nq * std::max(R, 1) * 4);
+  L.off_cand = off; off = al(off + (size_t)Nq * cand * 4);
+  L.off_ccnt = off; off = al(off + (size_t)(cand > 0 ? Nq : 0) * 4);
+  L.off_resc = off; off = al(off + (size_t)Nq * cand * 4);
   L.total = off;
   return L;
 }
 
 }  // namespace
 
-size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads) {
-  return idx_layout(Nq, Nk, Hi, route_heads).total;
+size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads, int cand) {
+  return idx_layout(Nq, Nk, Hi, route_heads, cand).total;
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
-  if (a.route_heads > 8) return hipErrorNotSupported;
-  IdxLayout L = idx_layout(a.Nq, a.Nk, a.Hi, a.route_heads);
+  if (a.route_heads > 8 || (a.cand > 0 && a.route_heads < 1)) return hipErrorNotSupported;
+  IdxLayout L = idx_layout(a.Nq, a.Nk, a.Hi, a.route_heads, a.cand);
   char* base = (char*)ws;
   float* scores = (float*)(base + L.off_scores);
   QkArgs q;
@@ -480,6 +576,20 @@ hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
     q.route = nullptr;
     q.R = 0;
     hipLaunchKernelGGL(qk_heads_kernel<MODE_DENSE>, dim3((a.Nq + NW - 1) / NW), dim3(NTI), 0, st, q);
+  }
+  if (a.cand > 0) {
+    // hierarchical: routed top-cand candidates, rescored by every head, top-k of them
+    int32_t* cidx = a.cand_idx ? a.cand_idx : (int32_t*)(base + L.off_cand);
+    int32_t* ccnt = a.cand_count ? a.cand_count : (int32_t*)(base + L.off_ccnt);
+    const int ccap = a.cand_idx ? a.cand_cap : a.cand;
+    float* resc = (float*)(base + L.off_resc);
+    hipLaunchKernelGGL(token_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, scores, a.Nq, a.Nk, a.q_offset, a.cand,
+                       cidx, ccnt, ccap);
+    hipLaunchKernelGGL(cand_score_kernel, dim3((a.Nq + CS_WAVES - 1) / CS_WAVES), dim3(CS_WAVES * 64), 0, st, a.q_idx,
+                       a.k_idx, a.w, cidx, ccnt, a.Nq, a.Hi, ccap, resc);
+    hipLaunchKernelGGL(cand_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, resc, cidx, ccnt, ccap, a.topk, a.tok,
+                       a.tok_count, a.tok_cap);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(token_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, scores, a.Nq, a.Nk, a.q_offset, a.topk, a.tok,
                      a.tok_count, a.tok_cap);

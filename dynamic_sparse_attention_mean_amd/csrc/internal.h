@@ -93,10 +93,15 @@ struct IndexerArgs {
   int Nq, Nk, Hi, q_offset, route_heads, topk;
   int32_t* tok; int32_t* tok_count; int tok_cap;
   int32_t* route;          // nullable [Nq, route_heads]
+  // hierarchical option (cand > 0): candidates per query, their list (nullable:
+  // workspace) with capacity cand_cap and counts
+  int cand;
+  int32_t* cand_idx; int32_t* cand_count; int cand_cap;
 };
-size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads);
+size_t indexer_workspace_bytes(int Nq, int Nk, int Hi, int route_heads, int cand);
 hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st);
 constexpr int kMaxTokensPerQuery = 4096;
+constexpr int kMaxCandidates = 65536;   // candidates per query of the hierarchical indexer
 // Attention of the TOKEN heads over per-query token lists.
 hipError_t launch_token_attention(const AttnArgs& a, hipStream_t st);
 

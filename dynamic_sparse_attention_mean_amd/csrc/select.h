@@ -295,16 +295,30 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
       if ((key & pmask) == prefix) atomicAdd(&sm.t.hist[(key >> sh) & dmask], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t run = 0u;
-      for (int d = (int)dmask; d >= 0; --d) {
-        const uint32_t c = sm.t.hist[d];
-        if (run + c >= (uint32_t)need) {
-          sm.t.scal[4] = (uint32_t)d;
-          sm.t.scal[5] = run;
-          break;
+    if (w == 0) {
+      // lane l owns digits dmask - 4l .. dmask - 4l - 3 (descending); the lane
+      // whose range holds the need-th key names the digit and the count above it
+      uint32_t c[4];
+      uint32_t s = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = (int)dmask - 4 * l - i;
+        c[i] = d >= 0 ? sm.t.hist[d] : 0u;
+        s += c[i];
+      }
+      const uint32_t incl = wave_incl_scan(s);
+      const uint32_t excl = incl - s;
+      if (excl < (uint32_t)need && incl >= (uint32_t)need) {
+        uint32_t run = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (run + c[i] >= (uint32_t)need) {
+            sm.t.scal[4] = (uint32_t)((int)dmask - 4 * l - i);
+            sm.t.scal[5] = run;
+            break;
+          }
+          run += c[i];
         }
-        run += c;
       }
     }
     __syncthreads();

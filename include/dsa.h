@@ -63,7 +63,7 @@ enum {
 
 enum { DSA_SELECT_TOPK = 0, DSA_SELECT_THRESHOLD = 1 };
 enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
-enum { DSA_OP_VS = 1, DSA_OP_BLOCK = 2, DSA_OP_TOKENS = 3, DSA_OP_ATTN = 4 };
+enum { DSA_OP_VS = 1, DSA_OP_BLOCK = 2, DSA_OP_TOKENS = 3, DSA_OP_ATTN = 4, DSA_OP_TOKENS_HIER = 5 };
 
 typedef struct dsa_shape {
   int32_t batch;       /* B  >= 1 */
@@ -117,6 +117,7 @@ const char* dsa_last_error(void);
  *   DSA_OP_VS:     {n_heads, last_q}
  *   DSA_OP_BLOCK:  {n_heads, block}
  *   DSA_OP_TOKENS: {n_idx_heads, route_heads, topk}
+ *   DSA_OP_TOKENS_HIER: {n_idx_heads, route_heads, cand, topk}
  *   DSA_OP_ATTN:   {} (none)
  * Writes the size to *bytes.  Sizes depend on shapes only, never on data. */
 dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t* params,
@@ -187,6 +188,25 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
                               const float* w, int32_t n_idx_heads, int32_t route_heads,
                               int32_t topk, dsa_token_index out, int32_t* route,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Hierarchical indexer token top-k ("MISA", section on how MISA works, the
+ * hierarchical variant: the router's few heads find a larger candidate list,
+ * then every indexer head checks only those candidates).
+ *   stage 1: H(i) = the route_heads routed heads and score_r[i, j] the routed
+ *     score, both as in build_index_tokens; C(i) = top-`cand` keys j <= p_i by
+ *     score_r (ties to the lower index);
+ *   stage 2: score[i, j] = sum over every head h of w[i, h] * max(0, q_idx[i, h]
+ *     . k_idx[j]) for j in C(i); tokens = top-`topk` of C(i) by it (ties to the
+ *     lower index), ascending, min(topk, |C(i)|) keys.
+ * Arguments as build_index_tokens, plus: route_heads in [1, 8]; topk <= 4096;
+ * cand in [topk, 65536]; cands (nullable, device, cap >= cand) receives C(i)
+ * ascending, otherwise C(i) lives in the workspace.  Workspace:
+ * dsa_workspace_size(DSA_OP_TOKENS_HIER, {n_idx_heads, route_heads, cand, topk}). */
+dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, const void* k_idx,
+                                   const float* w, int32_t n_idx_heads, int32_t route_heads,
+                                   int32_t cand, int32_t topk, dsa_token_index out,
+                                   const dsa_token_index* cands, int32_t* route,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Sparse prefill attention over each head's index set ("MInference 1.0"
  * explainer, GPU kernels: attention only at the indexed positions;

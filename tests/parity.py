@@ -182,3 +182,32 @@ def assert_attention_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
         if fin.any():
             assert np.abs(lse_gpu[fin] - lse_ref[fin]).max() <= MAX_ABS, f"{what}: LSE error"
     return float(err.max()), float(err.mean())
+
+
+def check_hier_row(qf_i, kf, wf_i, p, route, cand, topk, kbar, g_route, g_cands, g_tok, what=""):
+    """One query of the hierarchical indexer against the oracle's own stages.
+
+    The GPU's routing, candidates and final tokens are compared with the
+    oracle's, each within its cutoff band; no GPU result feeds the oracle.
+    Returns False when the GPU's routing or candidate choice fell inside a band
+    (the later stages then legitimately differ and are not compared)."""
+    Hi = qf_i.shape[0]
+    nc = (p + 1) // 64
+    best = (kbar[:nc] @ qf_i.T).max(axis=0) if nc else np.zeros(Hi)
+    r = wf_i * np.maximum(best, 0.0)
+    sel, c, tol = band_topk(r, np.arange(Hi), route)
+    assert_set_matches(g_route, r, sel, c, tol, expect_count=route, what=f"{what} route")
+    if set(int(x) for x in g_route) != sel:
+        return False
+    heads = np.array(sorted(sel))
+    routed = O.indexer_row(qf_i, kf, wf_i, p, heads)
+    sel1, c1, tol1 = band_topk(routed, np.arange(p + 1), cand)
+    assert_set_matches(g_cands, routed, sel1, c1, tol1, expect_count=min(cand, p + 1), what=f"{what} candidates")
+    if set(int(x) for x in g_cands) != sel1:
+        return False
+    members = np.array(sorted(sel1))
+    dense = np.full(p + 1, -np.inf)
+    dense[members] = O.indexer_row(qf_i, kf[members], wf_i, len(members) - 1)
+    sel2, c2, tol2 = band_topk(dense, members, topk)
+    assert_set_matches(g_tok, dense, sel2, c2, tol2, expect_count=min(topk, len(members)), what=f"{what} tokens")
+    return True

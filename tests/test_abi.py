@@ -168,3 +168,50 @@ def test_ashape_validation_paths():
     assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 4, 0, vs_c(), None) == dsa.DSA_ERR_INVALID_ARG
     assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 32, 8, vs_c(16, 16), None) == dsa.DSA_ERR_INVALID_ARG
     assert L.build_index_ashape(ctypes.byref(sh), heads, 1, 4, 8, vs_c(null=True), None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def tok_c(cap, null=False):
+    return dsa._TokenIndexC(None if null else FAKE, None if null else FAKE, cap)
+
+
+def test_tokens_validation_paths():
+    """Both indexer entry points reject bad budgets, head counts and index sets
+    on the host (the hierarchical one also its candidate count and list)."""
+    L = dsa.lib()
+    sh = shape(heads=1, kv_heads=1, q_len=64, kv_len=1024, q_offset=960)
+    st, need = ws_size(dsa.OP_TOKENS, sh, [64, 8, 100])
+    assert st == 0 and need >= 64 * 1024 * 4
+    st, need_h = ws_size(dsa.OP_TOKENS_HIER, sh, [64, 8, 400, 100])
+    assert st == 0 and need_h >= need + 2 * 64 * 400 * 4
+    assert ws_size(dsa.OP_TOKENS_HIER, sh, [64, 0, 400, 100])[0] == dsa.DSA_ERR_INVALID_ARG     # no routing
+    assert ws_size(dsa.OP_TOKENS_HIER, sh, [64, 8, 50, 100])[0] == dsa.DSA_ERR_INVALID_ARG      # cand < topk
+
+    def tok(**kw):
+        return L.build_index_tokens(ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, FAKE, kw.get("hi", 64),
+                                    kw.get("r", 8), kw.get("topk", 100), kw.get("out", tok_c(100)), None,
+                                    kw.get("ws", FAKE), kw.get("wsb", need), None)
+
+    assert tok(hi=65) == dsa.DSA_ERR_UNSUPPORTED
+    assert tok(r=9) == dsa.DSA_ERR_UNSUPPORTED
+    assert tok(topk=0) == dsa.DSA_ERR_INVALID_ARG
+    assert tok(out=tok_c(50)) == dsa.DSA_ERR_INVALID_ARG
+    assert tok(out=tok_c(100, null=True)) == dsa.DSA_ERR_INVALID_ARG
+    assert tok(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert tok(sh=shape(batch=2, heads=1, kv_heads=1, q_len=64, kv_len=1024, q_offset=960)) == dsa.DSA_ERR_UNSUPPORTED
+
+    def hier(**kw):
+        c = kw.get("cands")
+        return L.build_index_tokens_hier(ctypes.byref(sh), FAKE, FAKE, FAKE, kw.get("hi", 64), kw.get("r", 8),
+                                         kw.get("cand", 400), kw.get("topk", 100), kw.get("out", tok_c(100)),
+                                         ctypes.byref(c) if c is not None else None, None, FAKE,
+                                         kw.get("wsb", need_h), None)
+
+    assert hier(r=0) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(r=9, hi=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert hier(cand=99) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(cand=65537, topk=100) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(topk=4097, cand=5000, out=tok_c(4097)) == dsa.DSA_ERR_UNSUPPORTED
+    assert hier(out=tok_c(99)) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(cands=tok_c(399)) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(cands=tok_c(400, null=True)) == dsa.DSA_ERR_INVALID_ARG
+    assert hier(wsb=need_h - 1) == dsa.DSA_ERR_WORKSPACE
