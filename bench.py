@@ -53,6 +53,8 @@ WORKLOADS = {
                     "(16 heads)", lambda: synth.config(5)),
     "indexer128k-routed": ("indexer top-2048 over N=131072, 8 of 64 heads routed per query + token attention "
                            "(16 heads)", lambda: synth.config(5, route_heads=8)),
+    "indexer128k-mqa": ("indexer top-2048 over N=131072 for an 8192-query chunk (64 heads, dense) + token attention "
+                        "(16 heads sharing one K/V, MQA)", lambda: synth.config(5, kv_heads=1)),
     "indexer128k-hier": ("hierarchical indexer top-2048 over N=131072: 8 of 64 heads routed per query pick 8192 "
                          "candidates, all 64 heads rescore them + token attention (16 heads)",
                          lambda: synth.config(5, route_heads=8, cand=8192)),
@@ -179,8 +181,8 @@ def cpu_baseline_indexer(w, sample_queries=32, seed=0):
         sets.append(O.token_topk(sc, p, topk))
         t_index += time.perf_counter() - t0
     for h in range(H):
-        kk = to_f64(w.k[0, h])
-        vv = to_f64(w.v[0, h])
+        kk = to_f64(w.k[0, h // (H // Hkv)])
+        vv = to_f64(w.v[0, h // (H // Hkv)])
         q = to_f64(w.q[0, h][torch.from_numpy(rows)])
         t0 = time.perf_counter()
         O.attention_rows(q, kk, vv, list(range(len(rows))), sets)
@@ -329,7 +331,11 @@ def main():
             # the rescoring of the candidates by every head
             extra["indexer_flop"] += float(2 * 128 * qi.shape[1] * np.minimum(pos + 1, cand).sum())
         extra["indexer_tflops"] = round(extra["indexer_flop"] / (ms_index * 1e-3) / 1e12, 2)
-        extra["gather_bytes"] = n_sel * 2 * d * 2
+        # K and V rows gathered: once per head, or once per group of up to 16
+        # heads when 8 or more heads share a KV head (the grouped kernel)
+        rep = H // Hkv
+        n_gather = Hkv * math.ceil(rep / 16) if rep >= 8 else H
+        extra["gather_bytes"] = (n_sel // H) * n_gather * 2 * d * 2
         extra["token_attn_gbs"] = round(extra["gather_bytes"] / (ms_attn * 1e-3) / 1e9, 1)
     else:
         layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)

@@ -28,6 +28,10 @@
 //     share through LDS), and cand_select_kernel keeps the top-k of them.
 //   token_attn_kernel: per (query, head) softmax over the gathered token list on
 //     VALU; the grid is head-major so a head's K/V stays in the Infinity Cache.
+//   token_attn_group_kernel: heads that share a KV head (8 or more per KV head,
+//     MQA included) and the per-query token list: one wave gathers each token's
+//     K and V row once for up to 16 such heads and runs both products on
+//     v_mfma_f32_16x16x32_bf16.
 #include "common.h"
 #include "internal.h"
 #include "select.h"
@@ -44,6 +48,11 @@ constexpr int NTI = NW * 64;      // threads per workgroup
 enum { MODE_DENSE = 0, MODE_ROUTED = 1, MODE_ROUTER = 2 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 __device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
@@ -511,6 +520,176 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
   }
 }
 
+// ---------------------------------------------------------------- token attention, shared K/V
+// MISA's problem section: the main attention reads only the tokens the indexer
+// kept, one list per query for all heads.  When many heads share one KV head,
+// the K and V rows of a query's tokens serve every one of them: a wave takes
+// (query, up to 16 heads of one KV head) and gathers each row once.
+//   S^T = K Q^T   (keys x heads): A = 16 gathered K rows x 32 dims, straight
+//                 from global memory; B = the heads' q (kept in registers).
+//   O^T += V^T P^T (dims x heads): B = the lane's own bf16 weights; A = V^T,
+//                 read with ds_read_b64_tr_b16 from the wave's LDS copy of the
+//                 chunk's 32 V rows.  The keys along the K dimension are
+//                 ordered so that the score layout of the first product is the
+//                 weight layout of the second: lane (g, t) holds keys
+//                 16 kb + 4 g + i (kb = 0, 1; i = 0..3) of head t in both.
+constexpr int TG_WAVES = 4;
+constexpr int TG_VSTRIDE = 288;      // bytes per staged V row: 256 + 32, so 8 rows of a transposing read hit 64 banks
+constexpr int TG_MAXGROUPS = 128;
+
+__global__ __launch_bounds__(TG_WAVES * 64) void token_attn_group_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int H, int Hkv,
+    int Nq, int Nk, int B, const int32_t* __restrict__ tidx, const int32_t* __restrict__ tcount, int tcap, void* o,
+    float* lse, int out_f32, TokenGroups tg) {
+  __shared__ __align__(16) char s_v[TG_WAVES][32 * TG_VSTRIDE];
+  const int wv_ = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, t = l & 15, g = l >> 4;
+  const int gi = blockIdx.y;
+  const int h0 = tg.h0[gi], nh = tg.cnt[gi];
+  const int row = blockIdx.x * TG_WAVES + wv_;          // b * Nq + i
+  if (row >= B * Nq) return;
+  const int b = row / Nq, i = row % Nq;
+  const int kvh = h0 / (H / Hkv);
+  const uint16_t* kb = k + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
+  const uint16_t* vb = v + ((size_t)b * Hkv + kvh) * (size_t)Nk * 128;
+  const bool hok = t < nh;
+  u32x4 qf[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (hok) x = *(const u32x4*)(q + (((size_t)b * H + h0 + t) * Nq + i) * 128 + 32 * ds + 8 * g);
+    qf[ds] = x;
+  }
+  const int n = min(tcount[row], tcap);
+  const int32_t* tl = tidx + (size_t)row * tcap;
+  char* sv = s_v[wv_];
+  const uint32_t svb = (uint32_t)(uintptr_t)(lds_char_t*)sv;
+  const float scale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+  // one chunk of 32 tokens: K fragments (A operand of the scores) for keys
+  // 16 kb + t, and this lane's half of V row l / 2
+  struct Chunk {
+    u32x4 kf[2][4];
+    u32x4 vx[8];
+    bool kval[2];
+  };
+  auto token = [&](int x, bool& ok) {
+    int j = x < n ? tl[x] : -1;
+    ok = j >= 0 && j < Nk;
+    return ok ? j : 0;
+  };
+  auto load = [&](int c0, Chunk& c) {
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      bool ok;
+      const int j = token(c0 + 16 * kbk + t, ok);
+      c.kval[kbk] = ok;
+      const uint16_t* kr = kb + (size_t)j * 128 + 8 * g;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) c.kf[kbk][ds] = *(const u32x4*)(kr + 32 * ds);
+    }
+    bool ok;
+    const int j = token(c0 + (l >> 1), ok);
+    const uint16_t* vr = vb + (size_t)j * 128 + 64 * (l & 1);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) c.vx[cc] = *(const u32x4*)(vr + 8 * cc);
+  };
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  Chunk cur, nxt;
+  if (n > 0) load(0, cur);
+  for (int c0 = 0; c0 < n; c0 += 32) {
+    // stage this chunk's V rows (the wave's own LDS; its reads of the last
+    // chunk were issued before these writes, and LDS runs a wave's accesses in order)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      *(lds_u32x4_t*)(uintptr_t)(svb + (l >> 1) * TG_VSTRIDE + 128 * (l & 1) + 16 * cc) = cur.vx[cc];
+    if (c0 + 32 < n) load(c0 + 32, nxt);
+    // ---- scores: S^T[16 kb + 4 g + i][t]
+    f32x4 sc[2];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      sc[kbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        sc[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.kf[kbk][ds]),
+                                                           __builtin_bit_cast(bf16x8, qf[ds]), sc[kbk], 0, 0, 0);
+    }
+    // validity of the keys this lane's scores cover: key 16 kb + 4 g + i was
+    // loaded by lane 4 g + i (group 0)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      const uint32_t okb = (uint32_t)__builtin_amdgcn_ballot_w64(cur.kval[kbk]) & 0xFFFFu;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const bool ok = (okb >> (4 * g + ii)) & 1u;
+        sc[kbk][ii] = ok ? sc[kbk][ii] : -INFINITY;
+        mx = fmaxf(mx, sc[kbk][ii]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+    const bool grow = mx > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? mx : m_run;
+      const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;   // m_run = -inf gives 0
+      l_run *= f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= f;
+      m_run = mnew;
+    }
+    const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+    uint32_t pk[4];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int ii = 0; ii < 4; ii += 2) {
+        const uint32_t pb = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][ii], scale2, -muse)),
+                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][ii + 1], scale2, -muse)));
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
+        pk[2 * kbk + ii / 2] = pb;
+      }
+    const u32x4 bx = {pk[0], pk[1], pk[2], pk[3]};
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, bx);
+    // ---- O^T += V^T P^T: rows 4 g + t / 4 (keys 0..15) and 16 + 4 g + t / 4,
+    // four dims 16 db + 4 (t % 4) .. + 3 each
+    const uint32_t va = svb + (4 * g + (t >> 2)) * TG_VSTRIDE + 8 * (t & 3);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const short4_t ya = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)(va + 32 * db));
+      const short4_t yb =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)(va + 16 * TG_VSTRIDE + 32 * db));
+      const short8_t ab = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ab), pop, acc[db], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+  // ---- epilogue: head t's sum over the four lane groups; O = acc / l
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (!hok) return;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const size_t obase = (((size_t)b * H + h0 + t) * Nq + i) * 128;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int d = 16 * db + 4 * g;
+    const f32x4 ov = acc[db] * inv;
+    if (out_f32) {
+      *(f32x4*)((float*)o + obase + d) = ov;
+    } else {
+      u32x2 bv = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      *(u32x2*)((uint16_t*)o + obase + d) = bv;
+    }
+  }
+  if (g == 0 && lse)
+    lse[((size_t)b * H + h0 + t) * Nq + i] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+}
+
 struct IdxLayout {
   size_t off_scores, off_kbar, off_r, off_route, off_cand, off_ccnt, off_resc, total;
 };
@@ -603,6 +782,32 @@ hipError_t launch_token_attention(const AttnArgs& a, hipStream_t st) {
   for (int h = 0; h < a.H; ++h)
     if (a.kind[h] == 3) th.h[th.n++] = h;
   if (th.n == 0) return hipSuccess;
+  const int rep = a.H / a.Hkv;
+  if (rep >= 8) {
+    // runs of consecutive token heads of one KV head, at most 16 per group
+    TokenGroups tg;
+    tg.n = 0;
+    for (int x = 0; x < th.n && tg.n <= TG_MAXGROUPS; ++x) {
+      const int h = th.h[x];
+      const bool extend = tg.n > 0 && h == tg.h0[tg.n - 1] + tg.cnt[tg.n - 1] && h / rep == tg.h0[tg.n - 1] / rep &&
+                          tg.cnt[tg.n - 1] < 16;
+      if (extend) {
+        ++tg.cnt[tg.n - 1];
+      } else if (tg.n < TG_MAXGROUPS) {
+        tg.h0[tg.n] = h;
+        tg.cnt[tg.n] = 1;
+        ++tg.n;
+      } else {
+        tg.n = TG_MAXGROUPS + 1;                         // too many groups: per-head kernel below
+      }
+    }
+    if (tg.n <= TG_MAXGROUPS) {
+      hipLaunchKernelGGL(token_attn_group_kernel, dim3((unsigned)((a.B * a.Nq + TG_WAVES - 1) / TG_WAVES), tg.n),
+                         dim3(TG_WAVES * 64), 0, st, a.q, a.k, a.v, a.H, a.Hkv, a.Nq, a.Nk, a.B, a.tidx, a.tcount,
+                         a.tcap, a.o, a.lse, a.out_f32, tg);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(token_attn_kernel, dim3((unsigned)((size_t)th.n * a.B * a.Nq)), dim3(TA_THREADS), 0, st, a.q,
                      a.k, a.v, a.H, a.Hkv, a.Nq, a.Nk, a.tidx, a.tcount, a.tcap, a.o, a.lse, a.out_f32, a.B, th);
   return hipGetLastError();

@@ -13,6 +13,11 @@ struct HeadList {                    // small head lists travel as kernel argume
   int32_t n;
   int32_t h[256];
 };
+struct TokenGroups {                 // token heads h0 .. h0 + cnt - 1 of one KV head, cnt <= 16
+  int32_t n;
+  int32_t h0[128];
+  int32_t cnt[128];
+};
 
 // ----------------------------------------------------------------- pooling
 // dst[b][head][I][:] = bf16(mean of src[b][head][I*block .. ][:]) for the listed

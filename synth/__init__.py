@@ -223,19 +223,22 @@ def threshold_sweep(seed: int = 4, N: int = 4096, H: int = 32, Hkv: int = 8, blo
 # Workload 5: indexer-style token top-k on the last query chunk.
 # ---------------------------------------------------------------------------
 def indexer_chunk(seed: int = 5, N: int = 131072, Nq: int = 8192, Hi: int = 64, di: int = 128,
-                  H: int = 16, topk: int = 2048, route_heads: int = 0, cand: int = 0) -> Workload:
+                  H: int = 16, topk: int = 2048, route_heads: int = 0, cand: int = 0,
+                  kv_heads: Optional[int] = None) -> Workload:
     """q_idx [Nq, Hi, di], k_idx [N, di] bf16, w [Nq, Hi] fp32 ~ U(0,1), attention
     Q [1, H, Nq, d] and K, V [1, H, N, d]; everything N(0,1), nothing planted.
     The chunk is the last Nq positions: q_offset = N - Nq.  cand > 0 asks for
-    the hierarchical indexer with that many routed candidates per query."""
+    the hierarchical indexer with that many routed candidates per query;
+    kv_heads = 1 gives the attention one K/V shared by all heads (MQA)."""
     g = _gen(seed)
     q_idx = torch.randn(Nq, Hi, di, generator=g).to(torch.bfloat16).contiguous()
     k_idx = torch.randn(N, di, generator=g).to(torch.bfloat16).contiguous()
     w = torch.rand(Nq, Hi, generator=g).contiguous()
-    q, k, v = _qkv(g, 1, H, H, N, Nq=Nq)
+    q, k, v = _qkv(g, 1, H, H if kv_heads is None else kv_heads, N, Nq=Nq)
     q, k, v = _bf(q, k, v)
     plan = [HeadPlan(TOKEN) for _ in range(H)]
-    return Workload(f"indexer_N{N}_r{route_heads}" + (f"_c{cand}" if cand else ""), q, k, v, plan, q_offset=N - Nq,
+    name = f"indexer_N{N}_r{route_heads}" + (f"_c{cand}" if cand else "") + (f"_kv{kv_heads}" if kv_heads else "")
+    return Workload(name, q, k, v, plan, q_offset=N - Nq,
                     extra={"q_idx": q_idx, "k_idx": k_idx, "w": w, "topk": topk,
                            "route_heads": route_heads, "route_block": 64, "cand": cand})
 

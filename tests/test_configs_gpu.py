@@ -142,9 +142,9 @@ def test_config4_threshold_256k_sampled():
     check_rows(w, layer, o, lse, [0, 5, 10, 15, 20, 25, 31], rows_per_head=12)
 
 
-@pytest.mark.parametrize("route", [0, 8])
-def test_config5_indexer_128k(route):
-    w = synth.config(5, route_heads=route)
+@pytest.mark.parametrize("route,kv_heads", [(0, None), (8, None), (0, 1)])
+def test_config5_indexer_128k(route, kv_heads):
+    w = synth.config(5, route_heads=route, kv_heads=kv_heads)
     B, H, Hkv, Nq, Nk, d = w.shape
     qi, ki, wt = w.extra["q_idx"], w.extra["k_idx"], w.extra["w"]
     topk = w.extra["topk"]
@@ -189,8 +189,9 @@ def test_config5_indexer_128k(route):
         need = np.unique(np.concatenate(list(sets.values())))
         kk = np.zeros((Nk, d))
         vv = np.zeros((Nk, d))
-        kk[need] = f64(w.k[0, h][torch.from_numpy(need)])
-        vv[need] = f64(w.v[0, h][torch.from_numpy(need)])
+        kh = h // (H // Hkv)
+        kk[need] = f64(w.k[0, kh][torch.from_numpy(need)])
+        vv[need] = f64(w.v[0, kh][torch.from_numpy(need)])
         ref_o, _ = O.attention_rows(f64(w.q[0, h][torch.from_numpy(np.array(rows))]), kk, vv,
                                     list(range(len(rows))), [sets[i] for i in rows])
         err = np.abs(o[0, h, rows] - ref_o)

@@ -163,3 +163,40 @@ def test_hierarchical_token_sets(N, Nq, Hi, route, cand, topk):
         c_o = O.token_topk(O.indexer_row(qf[i], kf, wf[i], p, h_o), p, cand)
         assert check_hier_row(qf[i], kf, wf[i], p, route, cand, topk, kbar, h_o, c_o, final[i], what=f"self q{i}")
     assert band_rows <= max(2, Nq // 20), f"{band_rows} of {Nq} rows chose inside a band"
+
+
+@pytest.mark.parametrize("H,Hkv,N,Nq,k,kinds", [
+    (16, 1, 1000, 70, 300, "token"),      # MQA: one group of 16 heads
+    (16, 2, 700, 50, 90, "token"),        # 8 heads per KV head
+    (24, 1, 600, 40, 64, "token"),        # groups of 16 and 8
+    (16, 1, 513, 33, 600, "mixed"),       # token heads between dense heads: groups of one head
+])
+def test_token_attention_shared_kv(H, Hkv, N, Nq, k, kinds):
+    """Token attention where 8 or more heads share a KV head (the grouped
+    MFMA kernel), on oracle token sets with ragged counts, empty lists and a
+    last chunk shorter than 32 tokens, against the fp64 oracle."""
+    g = np.random.default_rng(H * N + Hkv)
+    q, kk, v = synth.random_qkv(N + H, 1, H, Hkv, N, Nq=Nq)
+    qo = N - Nq
+    tok = []
+    for i in range(Nq):
+        m = 0 if i % 13 == 7 else int(g.integers(1, min(k, i + qo + 1) + 1))
+        tok.append(np.sort(g.choice(i + qo + 1, m, replace=False)))
+    ti = dsa.TokenIndex.empty(1, Nq, k, DEV)
+    idx = ti.idx.cpu()
+    for i, t in enumerate(tok):
+        idx[0, i, :len(t)] = torch.from_numpy(t.astype(np.int32))
+    ti.idx.copy_(idx)
+    ti.count.copy_(torch.tensor([[len(t) for t in tok]], dtype=torch.int32))
+    hk = [dsa.TOKEN if (kinds == "token" or h % 2 == 0) else dsa.DENSE for h in range(H)]
+    o, lse = dsa.sparse_prefill_attn(q.to(DEV), kk.to(DEV), v.to(DEV), hk, tok=ti)
+    torch.cuda.synchronize()
+    rep = H // Hkv
+    for h in range(H):
+        kh = h // rep
+        if hk[h] == dsa.TOKEN:
+            ref_o, ref_l = O.attention_rows(f64(q[0, h]), f64(kk[0, kh]), f64(v[0, kh]), list(range(Nq)), tok)
+        else:
+            m = O.mask_dense(Nq, N, qo)
+            ref_o, ref_l = O.masked_attention(f64(q[0, h]), f64(kk[0, kh]), f64(v[0, kh]), m)
+        assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l, f"head {h}")
