@@ -90,7 +90,10 @@ size_t ws_block(const dsa_shape* s, int n_heads, int block) {
   return c.off + 256;
 }
 
-size_t ws_attn(const dsa_shape* s) { return align256(attn_workspace_bytes(s->batch, s->heads, s->kv_len)) + 256; }
+size_t ws_attn(const dsa_shape* s, int sblock = 0, int scap = 0) {
+  return align256(attn_workspace_bytes(s->batch, s->heads, s->q_len, s->kv_len, sblock, scap)) + 256;
+}
+bool block_size_ok(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 
 }  // namespace
 
@@ -122,7 +125,7 @@ dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t*
       *bytes = ws_vs(shape, params[0]);
       return DSA_OK;
     case DSA_OP_BLOCK:
-      if (!need(2) || params[0] < 1 || params[0] > shape->heads || (params[1] != 64 && params[1] != 128))
+      if (!need(2) || params[0] < 1 || params[0] > shape->heads || !block_size_ok(params[1]))
         return fail(DSA_ERR_INVALID_ARG, "BLOCK params");
       *bytes = ws_block(shape, params[0], params[1]);
       return DSA_OK;
@@ -138,7 +141,10 @@ dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t*
       *bytes = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, params[0], params[1], params[2])) + 256;
       return DSA_OK;
     case DSA_OP_ATTN:
-      *bytes = ws_attn(shape);
+      // optional {block, cap} of the block index set: blocks of 16 or 32 need room for merged tile lists
+      if (n_params >= 2 && params && (!block_size_ok(params[0]) || params[1] < 1))
+        return fail(DSA_ERR_INVALID_ARG, "ATTN params");
+      *bytes = n_params >= 2 && params ? ws_attn(shape, params[0], params[1]) : ws_attn(shape);
       return DSA_OK;
     default:
       return fail(DSA_ERR_INVALID_ARG, "unknown op %d", op);
@@ -215,7 +221,7 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
   HeadList hl;
   if ((st = check_heads(shape, heads, n_heads, hl))) return st;
   if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
-  if (block != 64 && block != 128) return fail(DSA_ERR_UNSUPPORTED, "block %d (64 or 128)", block);
+  if (!block_size_ok(block)) return fail(DSA_ERR_UNSUPPORTED, "block %d (16, 32, 64 or 128)", block);
   if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "the block rule needs q_offset == 0");
   if (mode != DSA_SELECT_TOPK && mode != DSA_SELECT_THRESHOLD) return fail(DSA_ERR_INVALID_ARG, "mode %d", mode);
   if (mode == DSA_SELECT_TOPK && topk < 0) return fail(DSA_ERR_INVALID_ARG, "topk < 0");
@@ -353,14 +359,14 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   }
   if (use[DSA_PATTERN_BLOCK]) {
     if (!blk || !blk->idx || !blk->count || blk->cap < 1) return fail(DSA_ERR_INVALID_ARG, "block heads need a block index set");
-    if (blk->block != 64 && blk->block != 128) return fail(DSA_ERR_UNSUPPORTED, "block size %d", blk->block);
+    if (!block_size_ok(blk->block)) return fail(DSA_ERR_UNSUPPORTED, "block size %d", blk->block);
     if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "block heads need q_offset == 0");
   }
   if (use[DSA_PATTERN_TOKEN]) {
     if (!tok || !tok->idx || !tok->count || tok->cap < 1) return fail(DSA_ERR_INVALID_ARG, "token heads need a token index set");
     if (tok->cap > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "more than %d tokens per query", kMaxTokensPerQuery);
   }
-  const size_t need = ws_attn(shape);
+  const size_t need = use[DSA_PATTERN_BLOCK] ? ws_attn(shape, blk->block, blk->cap) : ws_attn(shape);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
 
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;

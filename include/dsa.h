@@ -96,7 +96,7 @@ typedef struct dsa_block_index {
   int32_t* idx;          /* [B, H, nqb, cap] */
   int32_t* count;        /* [B, H, nqb] */
   int32_t  cap;
-  int32_t  block;        /* 64 or 128 */
+  int32_t  block;        /* 16, 32, 64 or 128 */
 } dsa_block_index;
 
 /* Token index set (device memory, caller-owned), one list per query shared by
@@ -118,7 +118,8 @@ const char* dsa_last_error(void);
  *   DSA_OP_BLOCK:  {n_heads, block}
  *   DSA_OP_TOKENS: {n_idx_heads, route_heads, topk}
  *   DSA_OP_TOKENS_HIER: {n_idx_heads, route_heads, cand, topk}
- *   DSA_OP_ATTN:   {} (none)
+ *   DSA_OP_ATTN:   {} (none), or {block, cap} of the block index set passed to
+ *                  sparse_prefill_attn (required for blocks of 16 or 32)
  * Writes the size to *bytes.  Sizes depend on shapes only, never on data. */
 dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t* params,
                               int32_t n_params, size_t* bytes);
@@ -158,7 +159,7 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k,
  *   mode DSA_SELECT_TOPK: top-`topk` of J in [0, I] minus forced blocks;
  *   mode DSA_SELECT_THRESHOLD: J with S[I, J] >= max_J' S[I, J'] + log_alpha;
  *   then the union with block 0 (force_first) and block I (force_diag).
- * block in {64, 128}; q_offset must be 0; out.cap >= the largest count (top-k:
+ * block in {16, 32, 64, 128}; q_offset must be 0; out.cap >= the largest count (top-k:
  * min(nqb, topk + forced); threshold: nqb).  Nullable outputs for inspection:
  * qbar ([B, H, nqb, d] bf16, indexed by head number, rows of listed heads
  * written), kbar ([B, Hkv, nkb, d] bf16, rows of the listed heads' KV heads
@@ -217,8 +218,11 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
  * head_kind: HOST int32 [H] of DSA_PATTERN_*; the index struct of every kind
  * used must be non-null (vs / blk / tok).  Rows with an empty M(i) get O = 0
  * and LSE = -inf.  out_dtype DSA_OUT_BF16 or DSA_OUT_F32 selects O's type
- * ([B, H, Nq, d]); lse (nullable) is float [B, H, Nq].  Workspace:
- * dsa_workspace_size(DSA_OP_ATTN, {}). */
+ * ([B, H, Nq, d]); lse (nullable) is float [B, H, Nq].  Block sets of 16 or 32
+ * ("Optimizing Mixture of Block Attention" explainer: small blocks; the pairs'
+ * lists are merged per 64-key tile inside the call).  Workspace:
+ * dsa_workspace_size(DSA_OP_ATTN, {}), or with {blk->block, blk->cap} when
+ * block heads are present (the size then covers small-block lists). */
 dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k,
                                const void* v, const int32_t* head_kind,
                                const dsa_vs_index* vs, const dsa_block_index* blk,

@@ -65,7 +65,12 @@ def test_workspace_sizes():
     st, big = ws_size(dsa.OP_ATTN, shape(q_len=4096, kv_len=4096), [])
     assert big > n
     assert ws_size(99, shape(), [])[0] == dsa.DSA_ERR_INVALID_ARG
-    assert ws_size(dsa.OP_BLOCK, shape(), [4, 32])[0] == dsa.DSA_ERR_INVALID_ARG
+    assert ws_size(dsa.OP_BLOCK, shape(), [4, 48])[0] == dsa.DSA_ERR_INVALID_ARG
+    # blocks of 16 / 32 take room for the merged tile lists in the attention workspace
+    st, n_small = ws_size(dsa.OP_ATTN, shape(), [16, 40])
+    assert st == 0 and n_small > n
+    assert ws_size(dsa.OP_ATTN, shape(), [64, 40]) == (0, n)
+    assert ws_size(dsa.OP_ATTN, shape(), [20, 40])[0] == dsa.DSA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -125,7 +130,7 @@ def test_block_validation_paths():
                                    kw.get("mode", 0), kw.get("topk", 2), ctypes.c_float(kw.get("la", -3.0)),
                                    kw.get("ff", 1), kw.get("fd", 1), kw.get("out", good), None, None, None,
                                    kw.get("ws", FAKE), kw.get("wsb", need), None)
-    assert call(block=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(block=48) == dsa.DSA_ERR_UNSUPPORTED
     assert call(mode=7) == dsa.DSA_ERR_INVALID_ARG
     assert call(topk=-1) == dsa.DSA_ERR_INVALID_ARG
     # nqb = 4: top-3 plus two forced blocks needs min(4, 5) = 4 slots

@@ -36,7 +36,9 @@ def all_rows_check(w, sets, o, lse, what):
 # Block rule: pooling (bit-exact), scores, selection
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("N,block,mode,force", [(1000, 64, "topk", True), (2048, 64, "topk", False),
-                                                (1100, 128, "thresh", False), (777, 64, "thresh", True)])
+                                                (1100, 128, "thresh", False), (777, 64, "thresh", True),
+                                                (1000, 32, "topk", True), (700, 16, "thresh", False),
+                                                (513, 16, "topk", False)])
 def test_block_index_parity(N, block, mode, force):
     w = synth.block_planted(seed=20 + N, H=3, Hkv=1, N=N, block=block, n_plant=3, mode=mode, topk=4, force=force)
     q, k, _ = dev(w)
@@ -118,9 +120,14 @@ def test_attention_mixed_on_oracle_indices(N):
     all_rows_check(w, sets, o, lse, f"mixed N={N}")
 
 
-@pytest.mark.parametrize("block,N", [(64, 1500), (128, 1500), (128, 2048)])
-def test_attention_block_on_oracle_indices(block, N):
-    w = synth.block_planted(seed=40 + block, H=2, Hkv=1, N=N, block=block, n_plant=3, mode="thresh", force=False)
+@pytest.mark.parametrize("block,N,mode", [(64, 1500, "thresh"), (128, 1500, "thresh"), (128, 2048, "thresh"),
+                                         (32, 1500, "thresh"), (32, 2048, "topk"), (16, 1000, "thresh"),
+                                         (16, 777, "topk")])
+def test_attention_block_on_oracle_indices(block, N, mode):
+    """Block heads on the oracle's block sets; blocks of 16 and 32 exercise the
+    per-pair merged tile lists (query blocks smaller than a wave's rows)."""
+    w = synth.block_planted(seed=40 + block, H=2, Hkv=1, N=N, block=block, n_plant=3, mode=mode, topk=5,
+                            force=mode == "topk")
     q, k, v = dev(w)
     sets = {(0, h): oracle_head_sets(w, 0, h) for h in range(2)}
     kinds, vsi, bi = upload_sets(w, sets, DEV)
