@@ -269,6 +269,46 @@ def traffic_record():
         return None
 
 
+def block_sweep(args, dev, stream):
+    """Block-size sweep on single planted keys (MoBA: the router's SNR grows as
+    sqrt(d / B)): the same data and the same key budget (1024 keys per query
+    block) for B = 16, 32, 64, 128.  Recall = planted keys in blocks before the
+    query block that the GPU's selection keeps, over all such keys; time = one
+    step of the layer (index build + attention).  One JSON line."""
+    sweep = []
+    for blk in (16, 32, 64, 128):
+        w = synth.token_planted(block=blk)
+        B, H, Hkv, Nq, Nk, d = w.shape
+        q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+        layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
+        phases = [lambda: layer.build_indices(q, k), lambda: layer.attention(q, k, v)]
+        ms_step, (ms_index, ms_attn), _ = time_steps(phases, args.steps, args.warmup, stream)
+        f_sel = 4 * d * selected_count_layer(layer, w)
+        idx = layer.blk_index.idx[0].cpu().numpy()
+        cnt = layer.blk_index.count[0].cpu().numpy()
+        hit = tot = 0
+        for h in range(H):
+            pb = w.extra["planted_keys"][h].numpy() // blk
+            for I in range(idx.shape[1]):
+                rel = pb[pb < I]
+                if rel.size:
+                    hit += int(np.isin(rel, idx[h, I, :cnt[h, I]]).sum())
+                    tot += int(rel.size)
+        sweep.append({"block": blk, "recall": round(hit / tot, 4), "snr_model": round(w.extra["alpha"] * math.sqrt(d / blk), 3),
+                      "ms_index": round(ms_index, 4), "ms_attn": round(ms_attn, 4), "ms_step": round(ms_step, 4),
+                      "effective_tflops": round(f_sel / (ms_step * 1e-3) / 1e12, 2),
+                      "density": round(f_sel / (2 * d * H * Nq * (Nq + 1)), 5)})
+        log(f"[bench] block {blk}: recall {sweep[-1]['recall']}, {ms_step:.3f} ms/step")
+        del layer
+        torch.cuda.synchronize()
+    rec = {"metric": "recall of planted keys and ms per layer against the block size", "unit": "ms", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "block-size sweep: 8 heads, N=32768, d=128, 64 single planted keys per head "
+                                  "(alpha 1), top-(1024 / B) blocks + first + diagonal", "name": "blocksweep32k",
+                      "sweep": sweep}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +318,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache steps (profiling runs: every launch is then a warm one)")
+    ap.add_argument("--block-sweep", action="store_true",
+                    help="only run the block-size sweep (recall of planted keys, time per block size) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -289,6 +331,9 @@ def main():
         copy_calibration()
         return
     dev = torch.device("cuda", 0)
+    if args.block_sweep:
+        block_sweep(args, dev, torch.cuda.current_stream(dev))
+        return
     desc, make = WORKLOADS[args.workload]
     log(f"[bench] generating {args.workload}")
     w = make()

@@ -319,7 +319,9 @@ __device__ __forceinline__ bool cursor_has_next(const Item& it, const Cursor& c)
   return c.n < it.nent;
 }
 
-// Produce entry c.n and advance.  Valid only while cursor_has_next().
+// Produce entry c.n and advance.  Valid only while cursor_has_next().  SMALL:
+// the call has block heads with blocks of 16 or 32 (merged tile lists).
+template <bool SMALL>
 __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   Entry e;
   e.cnt = 0;
@@ -327,7 +329,7 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   e.kind = 0;
   e.use = ~0u;
   const int n = c.n++;
-  if (it.kind == 2 && it.per == 0) {
+  if (SMALL && it.kind == 2 && it.per == 0) {
     e.kt = ldc(it.l0, n);
     e.use = (uint32_t)ldc(it.l1, n);
     e.flags = ((e.use & 0xFFFFu) ? 1 : 0) | ((e.use >> 16) ? 2 : 0);
@@ -414,6 +416,7 @@ static_assert(OFF_MISC + 8 * 4 <= LDS_BYTES, "LDS arena overflow");
 
 __device__ __forceinline__ int mod5(int u) { return ((u % NSLOT) + NSLOT) % NSLOT; }
 
+template <bool SMALL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_SIMD))) void attn_kernel(
     const AttnArgs a, const Sched sc) {
   __shared__ __align__(1024) char s_lds[LDS_BYTES];
@@ -829,7 +832,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
         }
         __syncthreads();                         // the slots are free for the gather phase
-      } else if (it.kind == 2 && a.block < TK) {
+      } else if (SMALL && it.kind == 2 && a.block < TK) {
         // small blocks: the merged tile list of this pair
         it.per = 0;
         const size_t slot = (size_t)it.bh * a.bm_npairs + p;
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         } else if (it.kind == 2) {
           // per == 2: one shared list; per == 1: the cursor merges two lists and
           // stops when both are exhausted (nent is only an upper bound)
-          it.nent = it.per == 2 ? 2 * it.n0 : (it.per == 0 ? it.n0 : it.n0 + it.n1);
+          it.nent = it.per == 2 ? 2 * it.n0 : ((SMALL && it.per == 0) ? it.n0 : it.n0 + it.n1);
         } else if (it.kind == 0) {
           it.nent = it.last_pos / TK + 1;
         }
@@ -907,7 +910,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         cur.flags = 0;
         bool have = cursor_has_next(it, cc);
         if (have) {
-          cur = cursor_next(it, cc);
+          cur = cursor_next<SMALL>(it, cc);
           issue_tile<false>(kbp, a.Nk, cur, s_cols, ring, w, l, off_k);
           issue_tile<true>(vbp, a.Nk, cur, s_cols, ring + TK * 256, w, l, off_v);
         }
@@ -921,7 +924,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           if (!((cur.flags >> ih) & 1) || (cur.kind == 0 && cur.kt * TK > P0w + TQ - 1) || R0w > it.last_pos)
             mode = M_SKIP;
           else if (cur.kind == 1) mode = M_GATHER;
-          else if (it.kind == 2 && it.per == 0) mode = M_QUARTERS;
+          else if (SMALL && it.kind == 2 && it.per == 0) mode = M_QUARTERS;
           else if (it.kind == 3)
             // unmasked if every key is causal and inside the window or the sink for all the wave's rows
             mode = (cur.kt * TK + TK - 1 <= R0w && (R0w + 31 - cur.kt * TK <= it.wlen - 1 || cur.kt * TK + TK <= it.wsink))
@@ -934,7 +937,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           nxt.flags = 0;
           const bool have_n = cursor_has_next(it, cc);
           if (have_n) {
-            nxt = cursor_next(it, cc);
+            nxt = cursor_next<SMALL>(it, cc);
             issue_tile<false>(kbp, a.Nk, nxt, s_cols, ring + (stage ^ 1) * 2 * TK * 256, w, l, off_k);
             issue_tile<true>(vbp, a.Nk, nxt, s_cols, ring + ((stage ^ 1) * 2 + 1) * TK * 256, w, l, off_v);
           }
@@ -956,7 +959,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const int cs = it.wsink - (cur.kt * TK + 32 * kb);
               const uint32_t insink = cs >= 32 ? ~0u : (cs <= 0 ? 0u : ((1u << cs) - 1u));
               M = causal_mask32(ktop) & (inwin | insink);
-            } else if (mode == M_QUARTERS) {
+            } else if (SMALL && mode == M_QUARTERS) {
               // the 16-key quarters this row's 16-row group uses, and causal
               const int qb16 = 4 * ih + 2 * wr + (qn >> 4);
               const uint32_t nib = cur.use >> (4 * qb16);
@@ -1203,7 +1206,11 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   const long items = (long)heads.size() * T2;
   long grid = std::min<long>(items, (long)cu_count() * 2);
   grid = std::max<long>(sc.nq, (grid / sc.nq) * sc.nq);
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)grid), dim3(NT), 0, st, a, sc);
+  bool small = false;
+  if (a.block > 0 && a.block < TK)
+    for (int h = 0; h < a.H; ++h) small = small || a.kind[h] == 2;
+  if (small) hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, st, a, sc);
+  else hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, st, a, sc);
   return hipGetLastError();
 }
 

@@ -148,6 +148,32 @@ def block_planted(seed: int = 2, B: int = 1, H: int = 8, N: int = 32768, block: 
     return Workload(f"block_{mode}_N{N}", q, k, v, plan, extra={"planted_blocks": planted})
 
 
+def token_planted(seed: int = 6, N: int = 32768, H: int = 8, block: int = 64, n_plant: int = 64,
+                  alpha: float = 1.0, budget: int = 1024) -> Workload:
+    """Single planted keys for the block-size sweep: per head a direction u_h
+    (RMS 1 per element) and `n_plant` distinct key positions whose keys get
+    += alpha u_h; every query gets += u_h.  A planted key adds alpha sqrt(d)
+    to its token logit; mean pooling over a block of B keys leaves alpha
+    sqrt(d) / B of it against pooled noise of about 1 / sqrt(B), a ratio of
+    alpha sqrt(d / B).  The data do not depend on `block`; the plan keeps the
+    same key budget for every block size: top-(budget / block) blocks plus the
+    first and the diagonal block."""
+    g = _gen(seed)
+    q, k, v = _qkv(g, 1, H, H, N)
+    planted = []
+    for h in range(H):
+        u = _direction(g)
+        pos = _distinct(g, n_plant, 0, N)
+        k[0, h, pos] += alpha * u
+        q[0, h] += u
+        planted.append(torch.sort(pos).values)
+    q, k, v = _bf(q, k, v)
+    plan = [HeadPlan(BLOCK, block=block, mode="topk", topk=max(1, budget // block), force_first=True,
+                     force_diag=True) for _ in range(H)]
+    return Workload(f"token_planted_N{N}_B{block}", q, k, v, plan,
+                    extra={"planted_keys": planted, "alpha": alpha, "budget": budget})
+
+
 # ---------------------------------------------------------------------------
 # Workload 3: mixed per-head patterns, GQA 32/8, N = 131072.
 # ---------------------------------------------------------------------------
