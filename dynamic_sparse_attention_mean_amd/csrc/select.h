@@ -194,8 +194,28 @@ __device__ int select_threshold(const float* __restrict__ sc, int lo, int hi, fl
 //      the last pass writes every key > T and those keys == T in index order.
 // If bin b holds more candidates than LDS has room for, the row falls back to
 // the digit-by-digit select_topk.  Candidates are [0, n); returns the count
-// (uniform across the workgroup), writes ascending indices to out.
+// (uniform across the workgroup), writes ascending indices to out.  A row that
+// starts on a 16-byte boundary is read four keys per lane (one dwordx4 load);
+// pass 3 then orders a lane's four keys after the lanes before it with wave
+// prefix sums.
 constexpr int kSel3Cap = 6144;     // candidates of the threshold bin kept in LDS
+
+// Keys j .. j + 3 of the row (those below `end`); a lane's four keys come
+// from one 16-byte load when all four are in range.
+__device__ __forceinline__ void sel_load4(const float* __restrict__ sc, int j, int end, uint32_t (&key)[4],
+                                          bool (&ok)[4]) {
+  if (j + 3 < end) {
+    const f32x4 x = *(const f32x4*)(sc + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { key[e] = f32_order_key(x[e]); ok[e] = true; }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ok[e] = j + e < end;
+      key[e] = ok[e] ? f32_order_key(sc[j + e]) : 0u;
+    }
+  }
+}
 
 template <int NTH>
 struct Select3Smem {
@@ -221,10 +241,21 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
     for (int j = tid; j < n; j += NTH) out[j] = j;
     return n;
   }
+  const bool vec = ((uintptr_t)sc & 15u) == 0;
   // ---- pass 1: 12-bit histogram
   for (int i = tid; i < 4096; i += NTH) sm.t.hist[i] = 0u;
   __syncthreads();
-  for (int j = tid; j < n; j += NTH) atomicAdd(&sm.t.hist[f32_order_key(sc[j]) >> 20], 1u);
+  if (vec) {
+    const int n4 = n >> 2;
+    for (int j4 = tid; j4 < n4; j4 += NTH) {
+      const f32x4 x = *(const f32x4*)(sc + 4 * j4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&sm.t.hist[f32_order_key(x[e]) >> 20], 1u);
+    }
+    for (int j = 4 * n4 + tid; j < n; j += NTH) atomicAdd(&sm.t.hist[f32_order_key(sc[j]) >> 20], 1u);
+  } else {
+    for (int j = tid; j < n; j += NTH) atomicAdd(&sm.t.hist[f32_order_key(sc[j]) >> 20], 1u);
+  }
   __syncthreads();
   if (w == 0) {
     // lane l owns bins 4095 - 64 l .. 4032 - 64 l (descending)
@@ -253,11 +284,43 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
     return select_topk<NTH>(sc, 0, n, -1, -1, k, out, sm.r);
   }
   // ---- pass 2: candidates of the threshold bin; keys above it per wave segment
-  const int seg = (n + NW - 1) / NW;
+  // (segments start on multiples of 4, so a segment's dwordx4 loads stay aligned)
+  const int seg = vec ? (((n + NW - 1) / NW + 3) & ~3) : (n + NW - 1) / NW;
   const int s0 = min(n, w * seg), s1 = min(n, (w + 1) * seg);
   if (tid == 0) sm.t.scal[3] = 0u;
   __syncthreads();
   uint32_t gt = 0u;
+  if (vec) {
+    uint32_t gl = 0u;
+    for (int j0 = s0; j0 < s1; j0 += 256) {
+      const int j = j0 + 4 * l;
+      uint32_t key[4];
+      bool ok[4];
+      sel_load4(sc, j, s1, key, ok);
+      uint32_t nc = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gl += (ok[e] && (key[e] >> 20) > bin) ? 1u : 0u;
+        nc += (ok[e] && (key[e] >> 20) == bin) ? 1u : 0u;
+      }
+      const uint32_t incl = wave_incl_scan(nc);
+      const uint32_t tot = __shfl(incl, 63, 64);
+      if (tot) {
+        uint32_t base = 0u;
+        if (l == 0) base = atomicAdd(&sm.t.scal[3], tot);
+        base = __shfl(base, 0, 64);
+        uint32_t pos = base + incl - nc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ok[e] && (key[e] >> 20) == bin) {
+            sm.t.ckey[pos] = key[e];
+            sm.t.cidx[pos] = j + e;
+            ++pos;
+          }
+      }
+    }
+    gt = wave_sum_u32(gl);
+  } else
   for (int j0 = s0; j0 < s1; j0 += 64) {
     const int j = j0 + l;
     uint32_t key = 0u;
@@ -346,6 +409,38 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
     eq_before += e2;
   }
   // ---- pass 3: write the selected keys of this wave's segment in index order
+  if (vec) {
+    for (int j0 = s0; j0 < s1; j0 += 256) {
+      const int j = j0 + 4 * l;
+      uint32_t key[4];
+      bool ok[4];
+      sel_load4(sc, j, s1, key, ok);
+      uint32_t ne = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ne += (ok[e] && key[e] == T) ? 1u : 0u;
+      const uint32_t e_incl = wave_incl_scan(ne);
+      const uint32_t e_tot = __shfl(e_incl, 63, 64);
+      uint32_t erank = eq_before + e_incl - ne;      // keys == T before this lane's first
+      bool take[4];
+      uint32_t nt = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool g = ok[e] && key[e] > T;
+        const bool q = ok[e] && key[e] == T;
+        take[e] = g || (q && (int)erank < need_eq);
+        erank += q ? 1u : 0u;
+        nt += take[e] ? 1u : 0u;
+      }
+      const uint32_t t_incl = wave_incl_scan(nt);
+      const uint32_t t_tot = __shfl(t_incl, 63, 64);
+      uint32_t opos = out_pos + t_incl - nt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (take[e]) out[opos++] = j + e;
+      out_pos += t_tot;
+      eq_before += e_tot;
+    }
+  } else
   for (int j0 = s0; j0 < s1; j0 += 64) {
     const int j = j0 + l;
     bool g = false, e = false;
