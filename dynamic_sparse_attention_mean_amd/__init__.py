@@ -276,7 +276,7 @@ def sparse_prefill_attn(q, k, v, head_kind, vs: Optional[VSIndex] = None, blk: O
     if lse is None and want_lse:
         lse = torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
     kinds = (ctypes.c_int32 * H)(*[int(x) for x in head_kind])
-    ws = _workspace(OP_ATTN, shape, [blk.block, blk.idx.shape[-1]] if blk is not None else [], q.device, ws)
+    ws = _workspace(OP_ATTN, shape, [], q.device, ws)
     vsc = vs.c() if vs is not None else None
     bc = blk.c() if blk is not None else None
     tc = tok.c() if tok is not None else None

@@ -90,9 +90,7 @@ size_t ws_block(const dsa_shape* s, int n_heads, int block) {
   return c.off + 256;
 }
 
-size_t ws_attn(const dsa_shape* s, int sblock = 0, int scap = 0) {
-  return align256(attn_workspace_bytes(s->batch, s->heads, s->q_len, s->kv_len, sblock, scap)) + 256;
-}
+size_t ws_attn(const dsa_shape* s) { return align256(attn_workspace_bytes(s->batch, s->heads, s->kv_len)) + 256; }
 bool block_size_ok(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 
 }  // namespace
@@ -141,10 +139,7 @@ dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t*
       *bytes = align256(indexer_workspace_bytes(shape->q_len, shape->kv_len, params[0], params[1], params[2])) + 256;
       return DSA_OK;
     case DSA_OP_ATTN:
-      // optional {block, cap} of the block index set: blocks of 16 or 32 need room for merged tile lists
-      if (n_params >= 2 && params && (!block_size_ok(params[0]) || params[1] < 1))
-        return fail(DSA_ERR_INVALID_ARG, "ATTN params");
-      *bytes = n_params >= 2 && params ? ws_attn(shape, params[0], params[1]) : ws_attn(shape);
+      *bytes = ws_attn(shape);
       return DSA_OK;
     default:
       return fail(DSA_ERR_INVALID_ARG, "unknown op %d", op);
@@ -366,7 +361,7 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
     if (!tok || !tok->idx || !tok->count || tok->cap < 1) return fail(DSA_ERR_INVALID_ARG, "token heads need a token index set");
     if (tok->cap > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "more than %d tokens per query", kMaxTokensPerQuery);
   }
-  const size_t need = use[DSA_PATTERN_BLOCK] ? ws_attn(shape, blk->block, blk->cap) : ws_attn(shape);
+  const size_t need = ws_attn(shape);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
 
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;

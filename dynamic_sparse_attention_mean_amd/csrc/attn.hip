@@ -56,7 +56,7 @@ constexpr int TK = 64;       // keys per key tile
 constexpr int NT = 256;      // 4 waves: two query tiles x two 32-row halves
 constexpr int GCAP = 2048;   // gathered columns staged per round
 
-enum { M_NONE = 0, M_CAUSAL = 1, M_WIN = 2, M_GATHER = 3, M_SKIP = 4, M_QUARTERS = 5 };
+enum { M_NONE = 0, M_CAUSAL = 1, M_WIN = 2, M_GATHER = 3, M_SKIP = 4 };
 
 struct Sched {
   int nq;                       // number of queues
@@ -111,58 +111,6 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
 // as the prefix counts #{e' in D : e' <= e}.  A head whose lists are exactly
 // cols = [0, S) and diags = [0, L) (the A-shape sets: sink S, local window L)
 // is marked as a window head: its mask is closed-form and runs on whole tiles.
-// Block heads with blocks of 16 or 32 (MoBA's small blocks): the lists of the
-// 128 / block query blocks of each query-tile pair merge into one ascending
-// list of 64-key tiles, each with a use word: bit 4 r + c <-> the pair's rows
-// 16 r .. 16 r + 15 use the tile's keys 16 c .. 16 c + 15.  One thread per
-// (batch, head, pair); the lists are ascending, so entries of one tile are
-// adjacent in each list.
-__global__ void blk_merge_kernel(AttnArgs a, BhList L, int npairs) {
-  const int x = blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= L.n * npairs) return;
-  const int bh = L.bh[x / npairs], p = x % npairs;
-  const int nsub = 2 * TQ / a.block;                       // query blocks per pair: 4 or 8
-  const int I0 = p * nsub;
-  const int32_t* lp[8];
-  int cnt[8], pos[8];
-  for (int q = 0; q < 8; ++q) {
-    const int I = I0 + q;
-    const bool ok = q < nsub && I < a.nqb;
-    lp[q] = a.bidx + ((size_t)bh * a.nqb + (ok ? I : 0)) * a.bcap;
-    cnt[q] = ok ? min(a.bcount[(size_t)bh * a.nqb + I], a.bcap) : 0;
-    pos[q] = 0;
-  }
-  const size_t slot = (size_t)bh * npairs + p;
-  int32_t* tiles = a.bm_tile + slot * a.bm_cap;
-  uint32_t* uses = a.bm_use + slot * a.bm_cap;
-  const int per_tile = TK / a.block;                        // blocks per 64-key tile: 2 or 4
-  auto tile_of = [&](int J) { return J >= 0 ? J / per_tile : -((per_tile - 1 - J) / per_tile); };
-  int n = 0;
-  while (true) {
-    int T = 0x7fffffff;
-    for (int q = 0; q < nsub; ++q)
-      if (pos[q] < cnt[q]) T = min(T, tile_of(lp[q][pos[q]]));
-    if (T == 0x7fffffff) break;
-    uint32_t use = 0u;
-    for (int q = 0; q < nsub; ++q) {
-      while (pos[q] < cnt[q]) {
-        const int J = lp[q][pos[q]];
-        if (tile_of(J) != T) break;
-        const int c = J - T * per_tile;                     // block within the tile
-        if (a.block == 32) use |= (3u << (2 * c)) * 0x11u << (8 * q);    // two 16-row groups, two 16-key quarters
-        else use |= 1u << (4 * q + c);
-        ++pos[q];
-      }
-    }
-    if (n < a.bm_cap) {
-      tiles[n] = T;
-      uses[n] = use;
-    }
-    ++n;
-  }
-  a.bm_cnt[slot] = min(n, a.bm_cap);
-}
-
 __global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, int ND) {
   const int bh = L.bh[blockIdx.x];
   const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
@@ -276,7 +224,6 @@ struct Entry {
   int kt;      // key tile index, or gather chunk index
   int cnt;     // valid keys of a gather chunk
   int flags;   // bit h: query tile h of the pair uses this entry
-  uint32_t use;  // small blocks: bit 4 r + c <-> rows 16 r.. of the pair use keys 16 c.. of the tile
 };
 
 struct Item {
@@ -285,8 +232,8 @@ struct Item {
   int wsink, wlen;
   // BLOCK
   const int32_t* l0;       // list of query block I0 (or of the shared block)
-  const int32_t* l1;       // list of query block I0 + 1 (block 64 only); small blocks: the use words
-  int n0, n1, per;         // per: key tiles per list entry (1, 2), or 0 for the merged small-block list
+  const int32_t* l1;       // list of query block I0 + 1 (block 64 only)
+  int n0, n1, per;
   // stream
   int nent, ngather;
 };
@@ -319,21 +266,14 @@ __device__ __forceinline__ bool cursor_has_next(const Item& it, const Cursor& c)
   return c.n < it.nent;
 }
 
-// Produce entry c.n and advance.  Valid only while cursor_has_next().  SMALL:
-// the call has block heads with blocks of 16 or 32 (merged tile lists).
-template <bool SMALL>
+// Produce entry c.n and advance.  Valid only while cursor_has_next().
 __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   Entry e;
   e.cnt = 0;
   e.flags = 3;
   e.kind = 0;
-  e.use = ~0u;
   const int n = c.n++;
-  if (SMALL && it.kind == 2 && it.per == 0) {
-    e.kt = ldc(it.l0, n);
-    e.use = (uint32_t)ldc(it.l1, n);
-    e.flags = ((e.use & 0xFFFFu) ? 1 : 0) | ((e.use >> 16) ? 2 : 0);
-  } else if (it.kind == 1) {
+  if (it.kind == 1) {
     e.kind = 1;
     e.kt = n;
     e.cnt = min(TK, it.ngather - n * TK);
@@ -833,12 +773,58 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         }
         __syncthreads();                         // the slots are free for the gather phase
       } else if (SMALL && it.kind == 2 && a.block < TK) {
-        // small blocks: the merged tile list of this pair
-        it.per = 0;
-        const size_t slot = (size_t)it.bh * a.bm_npairs + p;
-        it.l0 = a.bm_tile + slot * a.bm_cap;
-        it.l1 = (const int32_t*)(a.bm_use + slot * a.bm_cap);
-        it.n0 = min(ldc(a.bm_cnt, slot), a.bm_cap);
+        // Blocks of 16 or 32: each wave walks the lists of its own 32 rows (one
+        // list for block 32, two for block 16) 32 keys at a time through its
+        // own 16 KB slot of the arena, with no workgroup barrier: the pair's
+        // waves share no key blocks worth a joint step.
+        __syncthreads();                         // every wave has read the item number
+        const uint32_t wslot = (uint32_t)(w * SLOT);
+        if (R0w <= it.last_pos) {
+          const int Ia = R0w / a.block;
+          const int32_t* la = a.bidx + ((size_t)it.bh * a.nqb + Ia) * a.bcap;
+          const int na = min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ia), a.bcap);
+          const bool two = a.block == 16 && Ia + 1 < a.nqb && R0w + 16 < a.Nq;   // rows 16-31: the next query block
+          const int32_t* lb = two ? a.bidx + ((size_t)it.bh * a.nqb + Ia + 1) * a.bcap : la;
+          const int nb = two ? min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ia + 1), a.bcap) : 0;
+          const int sh = a.block == 16 ? 1 : 0;   // list entry J lies in 32-key unit J >> sh
+          constexpr int NONE = 0x7fffffff;
+          int ia = 0, ib = 0;
+          int ja = na > 0 ? ldc(la, 0) : NONE, jb = nb > 0 ? ldc(lb, 0) : NONE;
+          const uint32_t lslot = ring + wslot;
+          while (true) {
+            const int u = min(ja == NONE ? NONE : (ja >> sh), jb == NONE ? NONE : (jb >> sh));
+            if (u == NONE) break;
+            // the 16-key halves of unit u that rows 0-15 (ga) and rows 16-31 (gb) use
+            uint32_t ga = 0u, gb = 0u;
+            while (ja != NONE && (ja >> sh) == u) {
+              ga |= sh ? (1u << (ja & 1)) : 3u;
+              ++ia;
+              ja = ia < na ? ldc(la, ia) : NONE;
+            }
+            while (jb != NONE && (jb >> sh) == u) {
+              gb |= 1u << (jb & 1);
+              ++ib;
+              jb = ib < nb ? ldc(lb, ib) : NONE;
+            }
+            if (!sh) gb = ga;                    // block 32: one list for all 32 rows
+            if (u < 0) continue;                 // out-of-range block ids contribute nothing
+            // K and V rows 32 u .. 32 u + 31 (clamped into the key range) into the
+            // slot: instruction i fills rows 4 i .. 4 i + 3, lane l row 4 i + l / 16
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 4 * i + (l >> 4);
+              const int key = min(max(32 * u + r, 0), a.Nk - 1);
+              dma16(kbp + (size_t)key * 128 + swz_k(r, l & 15) * 8, lslot + i * 1024);
+              dma16(vbp + (size_t)key * 128 + swz_v(r, l & 15) * 8, lslot + 8192 + i * 1024);
+            }
+            wait_vm();
+            const uint32_t g = qn < 16 ? ga : gb;
+            uint32_t M = ((g & 1u) ? 0x0000FFFFu : 0u) | ((g & 2u) ? 0xFFFF0000u : 0u);
+            M &= causal_mask32(iq - 32 * u);
+            sub32(wslot, wslot + 8192, M);
+          }
+        }
+        it.kind = 4;                             // no tile steps for this item
       } else if (it.kind == 2) {
         it.per = a.block / TK;
         const int I0 = it.P0 / a.block;
@@ -852,6 +838,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       }
 
       for (;;) {
+        if (SMALL && it.kind == 4) break;
         if (it.kind == 1) {
           // stage this pair's columns j <= last_pos, except those every wave's
           // sub-blocks already cover; cov bit w marks a column wave w covered
@@ -898,7 +885,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         } else if (it.kind == 2) {
           // per == 2: one shared list; per == 1: the cursor merges two lists and
           // stops when both are exhausted (nent is only an upper bound)
-          it.nent = it.per == 2 ? 2 * it.n0 : ((SMALL && it.per == 0) ? it.n0 : it.n0 + it.n1);
+          it.nent = it.per == 2 ? 2 * it.n0 : it.n0 + it.n1;
         } else if (it.kind == 0) {
           it.nent = it.last_pos / TK + 1;
         }
@@ -910,7 +897,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         cur.flags = 0;
         bool have = cursor_has_next(it, cc);
         if (have) {
-          cur = cursor_next<SMALL>(it, cc);
+          cur = cursor_next(it, cc);
           issue_tile<false>(kbp, a.Nk, cur, s_cols, ring, w, l, off_k);
           issue_tile<true>(vbp, a.Nk, cur, s_cols, ring + TK * 256, w, l, off_v);
         }
@@ -924,7 +911,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           if (!((cur.flags >> ih) & 1) || (cur.kind == 0 && cur.kt * TK > P0w + TQ - 1) || R0w > it.last_pos)
             mode = M_SKIP;
           else if (cur.kind == 1) mode = M_GATHER;
-          else if (SMALL && it.kind == 2 && it.per == 0) mode = M_QUARTERS;
           else if (it.kind == 3)
             // unmasked if every key is causal and inside the window or the sink for all the wave's rows
             mode = (cur.kt * TK + TK - 1 <= R0w && (R0w + 31 - cur.kt * TK <= it.wlen - 1 || cur.kt * TK + TK <= it.wsink))
@@ -937,7 +923,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           nxt.flags = 0;
           const bool have_n = cursor_has_next(it, cc);
           if (have_n) {
-            nxt = cursor_next<SMALL>(it, cc);
+            nxt = cursor_next(it, cc);
             issue_tile<false>(kbp, a.Nk, nxt, s_cols, ring + (stage ^ 1) * 2 * TK * 256, w, l, off_k);
             issue_tile<true>(vbp, a.Nk, nxt, s_cols, ring + ((stage ^ 1) * 2 + 1) * TK * 256, w, l, off_v);
           }
@@ -959,12 +945,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const int cs = it.wsink - (cur.kt * TK + 32 * kb);
               const uint32_t insink = cs >= 32 ? ~0u : (cs <= 0 ? 0u : ((1u << cs) - 1u));
               M = causal_mask32(ktop) & (inwin | insink);
-            } else if (SMALL && mode == M_QUARTERS) {
-              // the 16-key quarters this row's 16-row group uses, and causal
-              const int qb16 = 4 * ih + 2 * wr + (qn >> 4);
-              const uint32_t nib = cur.use >> (4 * qb16);
-              M = (((nib >> (2 * kb)) & 1u) ? 0x0000FFFFu : 0u) | (((nib >> (2 * kb + 1)) & 1u) ? 0xFFFF0000u : 0u);
-              M &= causal_mask32(ktop);
             } else if (mode == M_GATHER) {
               // staged columns ascend: the keys <= iq are a prefix of the chunk
               const int base = cur.kt * TK + 32 * kb;
@@ -1067,30 +1047,11 @@ VsLayout vs_layout(int B, int H, int Nk) {
   return L;
 }
 
-// Merged tile lists of small-block heads: per (batch*head, pair) bm_cap tiles
-// and use words, and a count.
-struct BmLayout {
-  int npairs, cap;
-  size_t off_tile, off_use, off_cnt, words;
-};
-BmLayout bm_layout(size_t base_words, int B, int H, int Nq, int Nk, int sblock, int scap) {
-  BmLayout M;
-  M.npairs = ((Nq + TQ - 1) / TQ + 1) / 2;
-  M.cap = (sblock == 16 || sblock == 32) ? (int)std::min<long>((long)(2 * TQ / sblock) * scap, (Nk + TK - 1) / TK) : 0;
-  const size_t nslot = (size_t)B * H * M.npairs;
-  M.off_tile = base_words;
-  M.off_use = M.off_tile + nslot * M.cap;
-  M.off_cnt = M.off_use + nslot * M.cap;
-  M.words = M.cap > 0 ? 2 * nslot * M.cap + nslot : 0;
-  return M;
-}
-
 }  // namespace
 
-size_t attn_workspace_bytes(int B, int H, int Nq, int Nk, int sblock, int scap) {
+size_t attn_workspace_bytes(int B, int H, int Nk) {
   VsLayout L = vs_layout(B, H, Nk);
-  const size_t base = L.off_win + (size_t)B * H * 2;
-  return (base + bm_layout(base, B, H, Nq, Nk, sblock, scap).words) * 4 + 256;
+  return (L.off_win + (size_t)B * H * 2) * 4 + 256;
 }
 
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
@@ -1114,15 +1075,6 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   a.dle = (int32_t*)(base + L.off_dle);
   a.win = (int32_t*)(base + L.off_win);
   a.sw = L.sw; a.vw = L.vw; a.dw = L.dw; a.dcap = L.ND;
-  {
-    const BmLayout M = bm_layout(L.off_win + (size_t)a.B * a.H * 2, a.B, a.H, a.Nq, a.Nk, a.block < TK ? a.block : 0,
-                                 a.bcap);
-    a.bm_tile = (int32_t*)(base + M.off_tile);
-    a.bm_use = base + M.off_use;
-    a.bm_cnt = (int32_t*)(base + M.off_cnt);
-    a.bm_cap = M.cap;
-    a.bm_npairs = M.npairs;
-  }
 
   hipError_t e = launch_zero_u32(base, L.total_words, st);
   if (e != hipSuccess) return e;
@@ -1139,20 +1091,6 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  // small-block merge
-  if (a.block > 0 && a.block < TK) {
-    BhList bl;
-    bl.n = 0;
-    for (int b = 0; b < a.B; ++b)
-      for (int h = 0; h < a.H; ++h)
-        if (a.kind[h] == 2) bl.bh[bl.n++] = (int16_t)(b * a.H + h);
-    if (bl.n > 0) {
-      const int nthr = bl.n * a.bm_npairs;
-      hipLaunchKernelGGL(blk_merge_kernel, dim3((nthr + 63) / 64), dim3(64), 0, st, a, bl, a.bm_npairs);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
-
   // Queue assignment.  Each head's cost is estimated (key tiles over all its
   // query tiles); the Q heads that share a KV head go to the same queue, so
   // that the items running together on one XCD stream the same K/V tiles
@@ -1167,7 +1105,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
       if (kd < 0 || kd > 2) continue;
       double per;
       if (kd == 0) per = 0.5 * (a.Nk / (double)TK);
-      else if (kd == 2 && a.block < TK) per = std::min<double>(a.bm_cap, 0.5 * a.Nk / TK);
+      else if (kd == 2 && a.block < TK) per = std::min<double>(a.bcap * (32.0 / a.block), 0.5 * a.Nk / TK);
       else if (kd == 2) per = std::min<double>(a.bcap * (a.block / TK), 0.5 * a.Nk / TK);
       else per = std::min<double>(0.5 * a.Nk / TK, 2.0 * a.diags_cap / TK + 1 + a.cols_cap / (double)TK);
       heads.push_back({per * T, b * a.H + h});

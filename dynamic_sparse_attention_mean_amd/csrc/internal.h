@@ -82,16 +82,12 @@ struct AttnArgs {
                                      // cols = [0, sink), diags = [0, window) (else window = -1)
   // Block sets
   const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
-  // blocks of 16 or 32: per (batch*head, pair) merged tile lists (workspace)
-  int32_t* bm_tile; uint32_t* bm_use; int32_t* bm_cnt; int bm_cap, bm_npairs;
   // Token sets
   const int32_t* tidx; const int32_t* tcount; int tcap;
   // Scheduling
   int32_t* counters;                 // [kMaxQueues] work-queue heads (zeroed by the launcher)
 };
-// sblock / scap: the block size and list capacity of small-block heads (16 or
-// 32), else 0: their merged tile lists take extra workspace
-size_t attn_workspace_bytes(int B, int H, int Nq, int Nk, int sblock, int scap);
+size_t attn_workspace_bytes(int B, int H, int Nk);
 hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st);
 
 // --------------------------------------------------------------- indexer

@@ -62,8 +62,7 @@ class SparsePrefillLayer:
             for (blk, mode, topk, _, ff, fd) in self.blk:
                 cap = max(cap, nqb if mode == THRESHOLD else min(nqb, topk + int(ff) + int(fd)))
             self.blk_index = BlockIndex.empty(B, H, nqb, cap, block, device)
-        bp = [self.blk_index.block, self.blk_index.idx.shape[-1]] if self.blk_index is not None else []
-        ws = workspace_size(OP_ATTN, shape, bp)
+        ws = workspace_size(OP_ATTN, shape)
         for (lq, nv, ns), hs in self.vs.items():
             ws = max(ws, workspace_size(OP_VS, shape, [len(hs), lq]))
         for key, hs in self.blk.items():

@@ -118,8 +118,7 @@ const char* dsa_last_error(void);
  *   DSA_OP_BLOCK:  {n_heads, block}
  *   DSA_OP_TOKENS: {n_idx_heads, route_heads, topk}
  *   DSA_OP_TOKENS_HIER: {n_idx_heads, route_heads, cand, topk}
- *   DSA_OP_ATTN:   {} (none), or {block, cap} of the block index set passed to
- *                  sparse_prefill_attn (required for blocks of 16 or 32)
+ *   DSA_OP_ATTN:   {} (none)
  * Writes the size to *bytes.  Sizes depend on shapes only, never on data. */
 dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t* params,
                               int32_t n_params, size_t* bytes);
@@ -219,10 +218,9 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
  * used must be non-null (vs / blk / tok).  Rows with an empty M(i) get O = 0
  * and LSE = -inf.  out_dtype DSA_OUT_BF16 or DSA_OUT_F32 selects O's type
  * ([B, H, Nq, d]); lse (nullable) is float [B, H, Nq].  Block sets of 16 or 32
- * ("Optimizing Mixture of Block Attention" explainer: small blocks; the pairs'
- * lists are merged per 64-key tile inside the call).  Workspace:
- * dsa_workspace_size(DSA_OP_ATTN, {}), or with {blk->block, blk->cap} when
- * block heads are present (the size then covers small-block lists). */
+ * ("Optimizing Mixture of Block Attention" explainer: small blocks) are walked
+ * 32 keys at a time per 32 query rows.  Workspace:
+ * dsa_workspace_size(DSA_OP_ATTN, {}). */
 dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k,
                                const void* v, const int32_t* head_kind,
                                const dsa_vs_index* vs, const dsa_block_index* blk,

@@ -66,11 +66,6 @@ def test_workspace_sizes():
     assert big > n
     assert ws_size(99, shape(), [])[0] == dsa.DSA_ERR_INVALID_ARG
     assert ws_size(dsa.OP_BLOCK, shape(), [4, 48])[0] == dsa.DSA_ERR_INVALID_ARG
-    # blocks of 16 / 32 take room for the merged tile lists in the attention workspace
-    st, n_small = ws_size(dsa.OP_ATTN, shape(), [16, 40])
-    assert st == 0 and n_small > n
-    assert ws_size(dsa.OP_ATTN, shape(), [64, 40]) == (0, n)
-    assert ws_size(dsa.OP_ATTN, shape(), [20, 40])[0] == dsa.DSA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,code", [
