@@ -256,3 +256,16 @@ def test_config5_hierarchical_128k():
                                   rt[i].cpu().numpy(), cands.idx[0, i, :cands.count[0, i]].cpu().numpy(),
                                   out.idx[0, i, :out.count[0, i]].cpu().numpy(), what=f"q{i}")
     assert checked >= len(rows) - 2, f"only {checked} of {len(rows)} sampled rows without band choices"
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_block_sweep_32k_small_blocks(block):
+    """The block-size sweep's data at a small block size (N=32768, 8 heads,
+    top-(1024/B) + first + diagonal): selections against the oracle within the
+    band, sampled rows against the oracle's attention over its own sets."""
+    w = synth.token_planted(block=block)
+    layer, o, lse = run_layer(w)
+    heads = [0, 3, 7]
+    os_ = osets_of(w, heads)
+    check_sets(w, layer, heads, os_)
+    check_rows(w, layer, o, lse, heads, os_, rows_per_head=24)
