@@ -200,3 +200,33 @@ def test_token_attention_shared_kv(H, Hkv, N, Nq, k, kinds):
             m = O.mask_dense(Nq, N, qo)
             ref_o, ref_l = O.masked_attention(f64(q[0, h]), f64(kk[0, kh]), f64(v[0, kh]), m)
         assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l, f"head {h}")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 1)])
+def test_token_attention_batch2(H, Hkv):
+    """Token lists per (batch, query) with B = 2, for the per-head gather
+    kernel (one head per KV head) and the grouped kernel (16 heads sharing one
+    K/V): each batch's rows attend over their own lists and their own K/V."""
+    B, N, Nq, k = 2, 600, 48, 120
+    g = np.random.default_rng(100 + H)
+    q, kk, v = synth.random_qkv(200 + H, B, H, Hkv, N, Nq=Nq)
+    qo = N - Nq
+    tok = [[np.sort(g.choice(i + qo + 1, int(g.integers(1, k + 1)), replace=False)) for i in range(Nq)]
+           for _ in range(B)]
+    ti = dsa.TokenIndex.empty(B, Nq, k, DEV)
+    idx = ti.idx.cpu()
+    cnt = torch.zeros(B, Nq, dtype=torch.int32)
+    for b in range(B):
+        for i, t in enumerate(tok[b]):
+            idx[b, i, :len(t)] = torch.from_numpy(t.astype(np.int32))
+            cnt[b, i] = len(t)
+    ti.idx.copy_(idx)
+    ti.count.copy_(cnt)
+    o, lse = dsa.sparse_prefill_attn(q.to(DEV), kk.to(DEV), v.to(DEV), [dsa.TOKEN] * H, tok=ti)
+    torch.cuda.synchronize()
+    rep = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            ref_o, ref_l = O.attention_rows(f64(q[b, h]), f64(kk[b, h // rep]), f64(v[b, h // rep]), list(range(Nq)),
+                                            tok[b])
+            assert_attention_close(o[b, h].cpu().numpy(), lse[b, h].cpu().numpy(), ref_o, ref_l, f"b={b} head {h}")
