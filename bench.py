@@ -10,7 +10,12 @@ that whole pass (index build + attention) over inputs already resident in HBM.
 Other workloads (--workload) measure the remaining settings with the same
 protocol; they are reported alongside, the headline line is the default.
 
-Prints one JSON line (fields described in the design doc).
+Prints one JSON line: the metric and its value (effective TFLOP/s = selected
+work / step time), ms per step and per phase, the roofline record of the
+attention kernel (achieved rate, peak, fraction, copy-calibrated HBM traffic
+when the stored counter record matches the attention sources) and the fp64
+CPU oracle's rate on a bounded sample.  --block-sweep prints the block-size
+sweep instead.
 """
 import argparse
 import hashlib
@@ -324,8 +329,8 @@ def main():
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the hot path runs on one device's share of heads; --gpus {args.gpus} is "
-              f"not supported (how the path would shard is described in DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU: heads (KV groups) shard across GPUs with no exchange, so each GPU runs "
+              f"this step on its share; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
