@@ -449,16 +449,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
 
-      // One 32x32 sub-block: S^T = K Q^T over the 32 keys whose swizzled K rows
-      // start at kbase, online softmax under the mask M (bit c <-> key c of this
-      // lane's row), O^T += V^T P^T with the V rows at vbase.
-      auto sub32 = [&](uint32_t kofs, uint32_t vofs, uint32_t M) {
-        if (!row_ok) M = 0u;
-        if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) return;
-        const bool masked = __builtin_amdgcn_ballot_w64(M != ~0u) != 0;
-
-        // ---- S^T = K Q^T for these 32 keys (eight K fragments read first)
-        f32x16 sacc;
+      // ---- pieces of the online softmax over 32-key sub-blocks
+      // S^T = K Q^T for the 32 keys whose swizzled K rows start at kofs (the
+      // eight K fragments are read first).
+      auto qk32 = [&](uint32_t kofs, f32x16& sacc) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
         u32x4 kf[8];
@@ -471,22 +465,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         DSA_PRIO_LO();
-
-        // ---- mask (one wave-uniform branch), online softmax on raw scores
-        // (the scale is folded into exp2)
-        if (masked) {
-          const uint32_t mk = M >> (4 * hh);
+      };
+      // Scores of keys whose bit in M (bit c <-> key c of this lane's row) is
+      // clear become -inf (bit select).
+      auto mask32 = [&](f32x16& sacc, uint32_t M) {
+        const uint32_t mk = M >> (4 * hh);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int pos = 8 * (v >> 2) + (v & 3);
-            const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
-            sacc[v] = __uint_as_float((__float_as_uint(sacc[v]) & keep) | (0xff800000u & ~keep));
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int pos = 8 * (v >> 2) + (v & 3);
+          const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);   // all ones if kept
+          sacc[v] = __uint_as_float((__float_as_uint(sacc[v]) & keep) | (0xff800000u & ~keep));
         }
+      };
+      // Row maximum of the raw scores in this lane (the row's other half is in lane l ^ 32).
+      auto lane_max = [&](const f32x16& sacc) {
         float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
         for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sacc[v]), sacc[v + 1]);
-        mx = fmaxf(mx, sacc[15]);
+        return fmaxf(mx, sacc[15]);
+      };
+      // Fold in a new scaled row maximum: rows rescale lazily, only when the
+      // maximum grows by more than 8 (log2 units).  Returns the maximum the
+      // weights are taken against.
+      auto grow_to = [&](float mx) {
         {
           // rows live in lanes l and l ^ 32: swap halves and take the max
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -503,7 +504,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             for (int v = 0; v < 16; ++v) acc[db][v] *= f;
           m_run = mnew;
         }
-        const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+        return (m_run == -INFINITY) ? 0.f : m_run;
+      };
+      // bf16 weights exp2(s scale - muse) of one sub-block (the row sum takes
+      // the same rounded values), then O^T += V^T P^T with the V rows at vofs
+      // (two 16-key steps).
+      auto pv32 = [&](const f32x16& sacc, float muse, uint32_t vofs) {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         uint32_t pk[8];
 #pragma unroll
@@ -511,12 +517,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], scale2, -muse));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], scale2, -muse));
           const uint32_t pb = pack_bf16x2(p0, p1);
-          // the row sum uses the same bf16-rounded weights as the PV product
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
           pk[v >> 1] = pb;
         }
-
-        // ---- O^T += V^T P^T over these 32 keys (two 16-key steps)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
@@ -541,9 +544,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         }
       };
 
-      // Two 32x32 sub-blocks of one 64-key tile: both S^T products first, then
-      // one softmax over the 64 keys (one max, one rescale decision), then both
-      // PV products.
+      // One 32x32 sub-block: S^T over the 32 keys at kofs, the online softmax
+      // under the mask M, O^T += V^T P^T with the V rows at vofs.
+      auto sub32 = [&](uint32_t kofs, uint32_t vofs, uint32_t M) {
+        if (!row_ok) M = 0u;
+        if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) return;
+        f32x16 sacc;
+        qk32(kofs, sacc);
+        if (__builtin_amdgcn_ballot_w64(M != ~0u) != 0) mask32(sacc, M);
+        const float muse = grow_to(lane_max(sacc));
+        pv32(sacc, muse, vofs);
+      };
+
+      // Two 32x32 sub-blocks of one 64-key tile (the second at + 32 rows): both
+      // S^T products first, then one softmax over the 64 keys (one maximum, one
+      // rescale decision), then both PV products.
       auto sub64 = [&](uint32_t kofs, uint32_t vofs, uint32_t M0, uint32_t M1) {
         if (!row_ok) { M0 = 0u; M1 = 0u; }
         const bool r0 = __builtin_amdgcn_ballot_w64(M0 != 0u) != 0;
@@ -552,97 +567,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         f32x16 sa0, sa1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { sa0[v] = 0.f; sa1[v] = 0.f; }
-        if (r0) {
-          u32x4 kf[8];
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const lds_u32x4_t*)(uintptr_t)(kaddr[ks] + kofs);
-          DSA_PRIO_HI();
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sa0, 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-          DSA_PRIO_LO();
-        }
-        if (r1) {
-          u32x4 kf[8];
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const lds_u32x4_t*)(uintptr_t)(kaddr[ks] + kofs + 8192);
-          DSA_PRIO_HI();
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            sa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], sa1, 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-          DSA_PRIO_LO();
-        }
-        auto apply_mask = [&](f32x16& sa, uint32_t M) {
-          const uint32_t mk = M >> (4 * hh);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int pos = 8 * (v >> 2) + (v & 3);
-            const uint32_t keep = (uint32_t)((int32_t)(mk << (31 - pos)) >> 31);
-            sa[v] = __uint_as_float((__float_as_uint(sa[v]) & keep) | (0xff800000u & ~keep));
-          }
-        };
-        if (__builtin_amdgcn_ballot_w64(M0 != ~0u) != 0) apply_mask(sa0, M0);
-        if (__builtin_amdgcn_ballot_w64(M1 != ~0u) != 0) apply_mask(sa1, M1);
-        float mx = fmaxf(fmaxf(sa0[0], sa0[1]), sa0[2]);
-#pragma unroll
-        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sa0[v]), sa0[v + 1]);
-        mx = fmaxf(mx, sa0[15]);
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, sa1[v]), sa1[v + 1]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
-        }
-        const bool grow = mx > m_run + 8.0f;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-          const float mnew = grow ? mx : m_run;
-          const float f = grow ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
-          l_run *= f;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[db][v] *= f;
-          m_run = mnew;
-        }
-        const float muse = (m_run == -INFINITY) ? 0.f : m_run;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        auto pv = [&](const f32x16& sa, uint32_t vo) {
-          uint32_t pk[8];
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[v], scale2, -muse));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[v + 1], scale2, -muse));
-            const uint32_t pb = pack_bf16x2(p0, p1);
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb), ones, l_run, false);
-            pk[v >> 1] = pb;
-          }
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
-            short4_t ya[4], yb[4];
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              ya[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)(vaddr[db] + vo + 16 * s2 * 256));
-              yb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(uintptr_t)(vaddr[db] + vo + (16 * s2 + 8) * 256));
-            }
-            DSA_PRIO_HI();
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const short8_t ab = {ya[db][0], ya[db][1], ya[db][2], ya[db][3], yb[db][0], yb[db][1], yb[db][2], yb[db][3]};
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ab), bop, acc[db], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-            DSA_PRIO_LO();
-          }
-        };
-        if (r0) pv(sa0, vofs);
-        if (r1) pv(sa1, vofs + 8192);
+        if (r0) qk32(kofs, sa0);
+        if (r1) qk32(kofs + 8192, sa1);
+        // an absent half has M = 0 in every lane: masked to -inf
+        if (__builtin_amdgcn_ballot_w64(M0 != ~0u) != 0) mask32(sa0, M0);
+        if (__builtin_amdgcn_ballot_w64(M1 != ~0u) != 0) mask32(sa1, M1);
+        const float muse = grow_to(fmaxf(lane_max(sa0), lane_max(sa1)));
+        if (r0) pv32(sa0, muse, vofs);
+        if (r1) pv32(sa1, muse, vofs + 8192);
       };
 
       int gcursor = 0, gcount = 0;
