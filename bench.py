@@ -12,8 +12,9 @@ protocol; they are reported alongside, the headline line is the default.
 
 Prints one JSON line: the metric and its value (effective TFLOP/s = selected
 work / step time), ms per step and per phase, the roofline record of the
-attention kernel (achieved rate, peak, fraction, copy-calibrated HBM traffic
-when the stored counter record matches the attention sources) and the fp64
+attention kernel (achieved rate on the selected work, peak, fraction; when the
+stored counter record matches the attention sources, the copy-calibrated HBM
+traffic and the rate on the MFMA work the launch executes) and the fp64
 CPU oracle's rate on a bounded sample.  --block-sweep prints the block-size
 sweep instead.
 """
@@ -259,19 +260,41 @@ def copy_calibration(nbytes=1 << 30, reps=3):
           flush=True)
 
 
-def traffic_record():
-    """HBM bytes (read + written) per attention launch, from committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs scaled by the copy calibration, if they were
-    taken on the attention sources as they are now."""
+def counter_record():
+    """The committed rocprofv3 counter record of the attention launch on the
+    mixed128k layer, if it was taken on the attention sources as they are now."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("attn_src_sha256") != attn_src_digest():
-            return None
-        return rec["bytes_per_launch"]["total"]
+        return rec if rec.get("attn_src_sha256") == attn_src_digest() else None
     except Exception:
         return None
+
+
+def traffic_record():
+    """HBM bytes (read + written) per attention launch, from committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs scaled by the copy calibration, if they were
+    taken on the attention sources as they are now."""
+    rec = counter_record()
+    try:
+        return rec["bytes_per_launch"]["total"] if rec else None
+    except Exception:
+        return None
+
+
+def executed_record(ms_attn):
+    """MFMA work the attention launch executes (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+    512 FLOP, from the committed counter record) against the measured attention
+    time: the rate counted on executed rather than selected FLOPs."""
+    rec = counter_record()
+    try:
+        flop = rec["mfma_mops_bf16"] * rec["mfma_flop_per_mop"]
+    except Exception:
+        return None
+    tf = flop / (ms_attn * 1e-3) / 1e12
+    return {"flop": flop, "achieved": round(tf, 3), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "source": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per launch (profiles/attn_kernel_mixed128k_traffic.json)"}
 
 
 def block_sweep(args, dev, stream):
@@ -442,6 +465,8 @@ def main():
                            "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                            "traffic": traffic_record() if args.workload == "mixed128k" else None,
                            "kernel": "attn_kernel (sparse_prefill_attn)"}
+        if args.workload == "mixed128k":
+            rec["roofline"]["executed"] = executed_record(ms_attn)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         cb = cpu_baseline_indexer(w) if args.workload.startswith("indexer") else cpu_baseline(w)
