@@ -217,6 +217,33 @@ __device__ __forceinline__ void sel_load4(const float* __restrict__ sc, int j, i
   }
 }
 
+// Loads per lane a wave keeps in flight in the streaming passes.
+constexpr int kSelU = 4;
+
+// The kSelU 256-key chunks of a wave from jg on: whole chunks (all below
+// `end`) by one 16-byte load per lane, all issued before any is used; a
+// partial chunk is read key by key in sel_keys.
+__device__ __forceinline__ void sel_load_group(const float* __restrict__ sc, int jg, int end, int l,
+                                               f32x4 (&raw)[kSelU]) {
+#pragma unroll
+  for (int u = 0; u < kSelU; ++u) {
+    const int j0 = jg + 256 * u;
+    raw[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j0 + 256 <= end) raw[u] = *(const f32x4*)(sc + j0 + 4 * l);
+  }
+}
+
+// Order keys of this lane's four keys j .. j + 3 of the chunk at j0.
+__device__ __forceinline__ void sel_keys(const f32x4& raw, const float* __restrict__ sc, int j0, int j, int end,
+                                         uint32_t (&key)[4], bool (&ok)[4]) {
+  if (j0 + 256 <= end) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { key[e] = f32_order_key(raw[e]); ok[e] = true; }
+  } else {
+    sel_load4(sc, j, end, key, ok);
+  }
+}
+
 template <int NTH>
 struct Select3Smem {
   union {
@@ -232,7 +259,7 @@ struct Select3Smem {
 };
 
 template <int NTH>
-__device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int32_t* __restrict__ out,
+__device__ __forceinline__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int32_t* __restrict__ out,
                                  Select3Smem<NTH>& sm) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -246,8 +273,20 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
   for (int i = tid; i < 4096; i += NTH) sm.t.hist[i] = 0u;
   __syncthreads();
   if (vec) {
+    // kSelU loads per lane are issued before any is used: one load in flight
+    // per lane leaves a pass bound by memory latency, not bandwidth
     const int n4 = n >> 2;
-    for (int j4 = tid; j4 < n4; j4 += NTH) {
+    int j4 = tid;
+    for (; j4 + (kSelU - 1) * NTH < n4; j4 += kSelU * NTH) {
+      f32x4 x[kSelU];
+#pragma unroll
+      for (int u = 0; u < kSelU; ++u) x[u] = *(const f32x4*)(sc + 4 * (j4 + u * NTH));
+#pragma unroll
+      for (int u = 0; u < kSelU; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&sm.t.hist[f32_order_key(x[u][e]) >> 20], 1u);
+    }
+    for (; j4 < n4; j4 += NTH) {
       const f32x4 x = *(const f32x4*)(sc + 4 * j4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) atomicAdd(&sm.t.hist[f32_order_key(x[e]) >> 20], 1u);
@@ -292,31 +331,38 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
   uint32_t gt = 0u;
   if (vec) {
     uint32_t gl = 0u;
-    for (int j0 = s0; j0 < s1; j0 += 256) {
-      const int j = j0 + 4 * l;
-      uint32_t key[4];
-      bool ok[4];
-      sel_load4(sc, j, s1, key, ok);
-      uint32_t nc = 0u;
+    for (int jg = s0; jg < s1; jg += 256 * kSelU) {
+      f32x4 raw[kSelU];
+      sel_load_group(sc, jg, s1, l, raw);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gl += (ok[e] && (key[e] >> 20) > bin) ? 1u : 0u;
-        nc += (ok[e] && (key[e] >> 20) == bin) ? 1u : 0u;
-      }
-      const uint32_t incl = wave_incl_scan(nc);
-      const uint32_t tot = __shfl(incl, 63, 64);
-      if (tot) {
-        uint32_t base = 0u;
-        if (l == 0) base = atomicAdd(&sm.t.scal[3], tot);
-        base = __shfl(base, 0, 64);
-        uint32_t pos = base + incl - nc;
+      for (int u = 0; u < kSelU; ++u) {
+        const int j0 = jg + 256 * u;
+        if (j0 >= s1) break;
+        const int j = j0 + 4 * l;
+        uint32_t key[4];
+        bool ok[4];
+        sel_keys(raw[u], sc, j0, j, s1, key, ok);
+        uint32_t nc = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (ok[e] && (key[e] >> 20) == bin) {
-            sm.t.ckey[pos] = key[e];
-            sm.t.cidx[pos] = j + e;
-            ++pos;
-          }
+        for (int e = 0; e < 4; ++e) {
+          gl += (ok[e] && (key[e] >> 20) > bin) ? 1u : 0u;
+          nc += (ok[e] && (key[e] >> 20) == bin) ? 1u : 0u;
+        }
+        const uint32_t incl = wave_incl_scan(nc);
+        const uint32_t tot = __shfl(incl, 63, 64);
+        if (tot) {
+          uint32_t base = 0u;
+          if (l == 0) base = atomicAdd(&sm.t.scal[3], tot);
+          base = __shfl(base, 0, 64);
+          uint32_t pos = base + incl - nc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ok[e] && (key[e] >> 20) == bin) {
+              sm.t.ckey[pos] = key[e];
+              sm.t.cidx[pos] = j + e;
+              ++pos;
+            }
+        }
       }
     }
     gt = wave_sum_u32(gl);
@@ -410,35 +456,42 @@ __device__ int select_topk_3pass(const float* __restrict__ sc, int n, int k, int
   }
   // ---- pass 3: write the selected keys of this wave's segment in index order
   if (vec) {
-    for (int j0 = s0; j0 < s1; j0 += 256) {
-      const int j = j0 + 4 * l;
-      uint32_t key[4];
-      bool ok[4];
-      sel_load4(sc, j, s1, key, ok);
-      uint32_t ne = 0u;
+    for (int jg = s0; jg < s1; jg += 256 * kSelU) {
+      f32x4 raw[kSelU];
+      sel_load_group(sc, jg, s1, l, raw);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ne += (ok[e] && key[e] == T) ? 1u : 0u;
-      const uint32_t e_incl = wave_incl_scan(ne);
-      const uint32_t e_tot = __shfl(e_incl, 63, 64);
-      uint32_t erank = eq_before + e_incl - ne;      // keys == T before this lane's first
-      bool take[4];
-      uint32_t nt = 0u;
+      for (int u = 0; u < kSelU; ++u) {
+        const int j0 = jg + 256 * u;
+        if (j0 >= s1) break;
+        const int j = j0 + 4 * l;
+        uint32_t key[4];
+        bool ok[4];
+        sel_keys(raw[u], sc, j0, j, s1, key, ok);
+        uint32_t ne = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool g = ok[e] && key[e] > T;
-        const bool q = ok[e] && key[e] == T;
-        take[e] = g || (q && (int)erank < need_eq);
-        erank += q ? 1u : 0u;
-        nt += take[e] ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) ne += (ok[e] && key[e] == T) ? 1u : 0u;
+        const uint32_t e_incl = wave_incl_scan(ne);
+        const uint32_t e_tot = __shfl(e_incl, 63, 64);
+        uint32_t erank = eq_before + e_incl - ne;      // keys == T before this lane's first
+        bool take[4];
+        uint32_t nt = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool g = ok[e] && key[e] > T;
+          const bool q = ok[e] && key[e] == T;
+          take[e] = g || (q && (int)erank < need_eq);
+          erank += q ? 1u : 0u;
+          nt += take[e] ? 1u : 0u;
+        }
+        const uint32_t t_incl = wave_incl_scan(nt);
+        const uint32_t t_tot = __shfl(t_incl, 63, 64);
+        uint32_t opos = out_pos + t_incl - nt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (take[e]) out[opos++] = j + e;
+        out_pos += t_tot;
+        eq_before += e_tot;
       }
-      const uint32_t t_incl = wave_incl_scan(nt);
-      const uint32_t t_tot = __shfl(t_incl, 63, 64);
-      uint32_t opos = out_pos + t_incl - nt;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (take[e]) out[opos++] = j + e;
-      out_pos += t_tot;
-      eq_before += e_tot;
     }
   } else
   for (int j0 = s0; j0 < s1; j0 += 64) {
