@@ -59,6 +59,10 @@ __device__ __forceinline__ void dma16(const void* g, lds_void_t* lds_base) {
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
+// max(0, x) for every finite x in one instruction: the median of x, 0 and the
+// largest finite float (v_med3_f32).  fmaxf(x, 0) costs two (a canonicalising
+// max of x with itself first), and a median against +inf is folded back into it.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.40282347e38f); }
 
 struct QkArgs {
   const uint16_t* q_idx;     // [Nq, Hi, 128]
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(NTI) void qk_heads_kernel(const QkArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = MODE == MODE_ROUTED ? (v >> 2) : 0;   // query of row 8 (v >> 2) + ...
-            s[j] = __builtin_fmaf(wv[hb][v], fmaxf(c[hb][v], 0.f), s[j]);
+            s[j] = __builtin_fmaf(wv[hb][v], relu(c[hb][v]), s[j]);
           }
 #pragma unroll
         for (int j = 0; j < QPW; ++j) {
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_score_kernel(const uint16_
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc = __builtin_fmaf(wv[hb][v], fmaxf(c[hb][v], 0.f), sacc);
+      for (int v = 0; v < 16; ++v) sacc = __builtin_fmaf(wv[hb][v], relu(c[hb][v]), sacc);
     const float tot = sacc + __shfl_xor(sacc, 32, 64);
     const int col = 32 * b + qn;
     if (hh == 0 && col < n) oq[col] = tot;
