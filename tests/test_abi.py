@@ -73,6 +73,10 @@ def test_workspace_sizes():
     (dict(heads=5), dsa.DSA_ERR_INVALID_ARG),
     (dict(q_len=100), dsa.DSA_ERR_INVALID_ARG),
     (dict(batch=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_len=0, kv_len=0), dsa.DSA_ERR_INVALID_ARG),      # empty input: rejected, not run
+    (dict(q_len=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(kv_heads=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(kv_len=1 << 30, q_len=1 << 30), dsa.DSA_ERR_INVALID_ARG),   # beyond the largest key count
     (dict(q_offset=-1, q_len=257), dsa.DSA_ERR_INVALID_ARG),
     (dict(heads=512, kv_heads=1), dsa.DSA_ERR_UNSUPPORTED),
 ])
