@@ -177,17 +177,33 @@ __global__ __launch_bounds__(256) void vs_pass2_kernel(VsScoreArgs a) {
       s_p[r * 65 + cc] = ok ? __builtin_amdgcn_exp2f(acc[v] * kScale2 - mr) * il : 0.f;
     }
     __syncthreads();
-    if (tid < 64) {
+    {
+      // column sums: four lanes per column, 16 rows each, then (p0 + p1) + (p2 + p3)
+      const int col = tid >> 2, part = tid & 3;
       float cs = 0.f;
-      for (int rr = 0; rr < 64; ++rr) cs += s_p[rr * 65 + tid];
-      if (kt * 64 + tid < a.Nk) vo[kt * 64 + tid] = cs;
-    } else if (tid < 64 + 127) {
-      const int dl = tid - 64 - 63;                // r - c
-      float ds = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cs += s_p[(16 * part + i) * 65 + col];
+      cs += __shfl_xor(cs, 1, 64);
+      cs += __shfl_xor(cs, 2, 64);
+      if (part == 0 && kt * 64 + col < a.Nk) vo[kt * 64 + col] = cs;
+    }
+    // diagonal sums: two lanes per diagonal dl = r - c (lower and upper rows of
+    // its range), then their sum; lanes 254 and 255 idle
+    {
+      const int dg = tid >> 1, part = tid & 1;
+      const int dl = min(dg, 126) - 63;
       const int rlo = max(0, dl), rhi = min(63, 63 + dl);
-      for (int rr = rlo; rr <= rhi; ++rr) ds += s_p[rr * 65 + (rr - dl)];
-      const int o = a.Nk - a.last_q - kt * 64 + dl;
-      s_diag[o - o_min] += ds;
+      const int rmid = (rlo + rhi + 1) >> 1;
+      float ds = 0.f;
+      if (dg < 127) {
+        const int r0 = part ? rmid : rlo, r1 = part ? rhi + 1 : rmid;
+        for (int rr = r0; rr < r1; ++rr) ds += s_p[rr * 65 + (rr - dl)];
+      }
+      ds += __shfl_xor(ds, 1, 64);
+      if (dg < 127 && part == 0) {
+        const int o = a.Nk - a.last_q - kt * 64 + dl;
+        s_diag[o - o_min] += ds;
+      }
     }
     __syncthreads();
   }
