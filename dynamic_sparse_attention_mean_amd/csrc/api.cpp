@@ -36,6 +36,14 @@ dsa_status hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Every workspace size carries 256 bytes of slack, so the carving can start at
+// the first 256-byte boundary of whatever the caller passed.
+void* ws_base(void* ws) { return ws ? (void*)(((uintptr_t)ws + 255) & ~(uintptr_t)255) : nullptr; }
+
+// Q, K, V, O and the indexer's q_idx / k_idx rows are read and written with
+// 16-byte vector accesses and LDS DMA.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 dsa_status check_shape(const dsa_shape* s) {
   if (!s) return fail(DSA_ERR_INVALID_ARG, "shape is null");
   if (s->batch < 1 || s->heads < 1 || s->kv_heads < 1 || s->q_len < 1 || s->kv_len < 1)
@@ -68,7 +76,7 @@ dsa_status check_heads(const dsa_shape* s, const int32_t* heads, int32_t n, Head
 struct WsCarver {
   char* base;
   size_t off = 0;
-  explicit WsCarver(void* p) : base((char*)p) {}
+  explicit WsCarver(void* p) : base((char*)ws_base(p)) {}
   template <class T>
   T* take(size_t count) {
     T* p = base ? (T*)(base + off) : nullptr;
@@ -172,6 +180,7 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k, 
   HeadList hl;
   if ((st = check_heads(shape, heads, n_heads, hl))) return st;
   if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
   if (last_q < 1 || last_q > 64 || last_q > shape->q_len) return fail(DSA_ERR_INVALID_ARG, "last_q out of range");
   if (nv < 0 || ns < 0 || nv > shape->kv_len || ns > shape->kv_len) return fail(DSA_ERR_INVALID_ARG, "budgets out of range");
   if (!out.cols || !out.cols_count || !out.diags || !out.diags_count)
@@ -216,6 +225,7 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
   HeadList hl;
   if ((st = check_heads(shape, heads, n_heads, hl))) return st;
   if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
   if (!block_size_ok(block)) return fail(DSA_ERR_UNSUPPORTED, "block %d (16, 32, 64 or 128)", block);
   if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "the block rule needs q_offset == 0");
   if (mode != DSA_SELECT_TOPK && mode != DSA_SELECT_THRESHOLD) return fail(DSA_ERR_INVALID_ARG, "mode %d", mode);
@@ -268,6 +278,7 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   dsa_status st = check_shape(shape);
   if (st) return st;
   if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx or w is null");
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
   if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 0 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
@@ -289,7 +300,7 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   a.route_heads = route_heads; a.topk = topk;
   a.tok = out.idx; a.tok_count = out.count; a.tok_cap = out.cap;
   a.route = route;
-  return hip_status(launch_indexer(a, ws, (hipStream_t)stream), "build_index_tokens");
+  return hip_status(launch_indexer(a, ws_base(ws), (hipStream_t)stream), "build_index_tokens");
 }
 
 dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, const void* k_idx, const float* w,
@@ -300,6 +311,7 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
   dsa_status st = check_shape(shape);
   if (st) return st;
   if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx or w is null");
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
   if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 1 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
@@ -327,7 +339,7 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
   a.cand_idx = cands ? cands->idx : nullptr;
   a.cand_count = cands ? cands->count : nullptr;
   a.cand_cap = cands ? cands->cap : cand;
-  return hip_status(launch_indexer(a, ws, (hipStream_t)stream), "build_index_tokens_hier");
+  return hip_status(launch_indexer(a, ws_base(ws), (hipStream_t)stream), "build_index_tokens_hier");
 }
 
 dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
@@ -338,6 +350,8 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   dsa_status st = check_shape(shape);
   if (st) return st;
   if (!q || !k || !v || !o) return fail(DSA_ERR_INVALID_ARG, "q, k, v or o is null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(DSA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (!head_kind) return fail(DSA_ERR_INVALID_ARG, "head_kind is null");
   if (out_dtype != DSA_OUT_BF16 && out_dtype != DSA_OUT_F32) return fail(DSA_ERR_INVALID_ARG, "out_dtype");
   AttnArgs a;
@@ -379,7 +393,7 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   if (use[DSA_PATTERN_TOKEN]) {
     a.tidx = tok->idx; a.tcount = tok->count; a.tcap = tok->cap;
   }
-  return hip_status(launch_attention(a, ws, (hipStream_t)stream), "sparse_prefill_attn");
+  return hip_status(launch_attention(a, ws_base(ws), (hipStream_t)stream), "sparse_prefill_attn");
 }
 
 }  // extern "C"

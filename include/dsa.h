@@ -18,7 +18,11 @@
  *  - Tensor arguments are device pointers owned by the caller.  The library
  *    does not allocate device memory, free it, or keep a pointer after the
  *    call returns.  Scratch memory comes from a caller-provided workspace
- *    whose size dsa_workspace_size() reports.
+ *    whose size dsa_workspace_size() reports.  The size includes 256 bytes
+ *    of slack, so the workspace pointer needs no particular alignment.
+ *  - Q, K, V, O and the indexer's q_idx and k_idx must be 16-byte aligned
+ *    (they are read and written with 16-byte accesses); a misaligned pointer
+ *    returns DSA_ERR_INVALID_ARG.
  *  - Arguments are checked on the host before any HIP call.  Kernels are then
  *    enqueued on `stream` (a hipStream_t; NULL means the default stream) and
  *    the call returns without synchronising.  Errors during execution show up

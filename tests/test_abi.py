@@ -162,6 +162,7 @@ def test_attention_validation_paths():
     assert call(kinds=(ctypes.c_int32 * 4)(0, 3, 0, 0)) in (dsa.DSA_ERR_INVALID_ARG, dsa.DSA_ERR_UNSUPPORTED)
     assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
     assert call(sh=shape(head_dim=96)) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(v=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG      # rows need 16-byte alignment
 
 
 def test_ashape_validation_paths():
@@ -196,6 +197,8 @@ def test_tokens_validation_paths():
                                     kw.get("ws", FAKE), kw.get("wsb", need), None)
 
     assert tok(hi=65) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.build_index_tokens(ctypes.byref(sh), ctypes.c_void_p(0x1002), FAKE, FAKE, 64, 8, 100, tok_c(100), None,
+                                FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG   # q_idx not 16-byte aligned
     assert tok(r=9) == dsa.DSA_ERR_UNSUPPORTED
     assert tok(topk=0) == dsa.DSA_ERR_INVALID_ARG
     assert tok(out=tok_c(50)) == dsa.DSA_ERR_INVALID_ARG
