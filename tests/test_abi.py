@@ -222,3 +222,14 @@ def test_tokens_validation_paths():
     assert hier(cands=tok_c(399)) == dsa.DSA_ERR_INVALID_ARG
     assert hier(cands=tok_c(400, null=True)) == dsa.DSA_ERR_INVALID_ARG
     assert hier(wsb=need_h - 1) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU and says so for --gpus above 1 (before any GPU work)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
