@@ -439,11 +439,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         if (row_ok) x = *(const u32x4*)(qbp + (size_t)qrow * 128 + 16 * ks + 8 * hh);
         qf[ks] = __builtin_bit_cast(bf16x8, x);
       }
-      // Take the Q fragments in before the tile loop: otherwise the compiler
-      // waits for these loads at their first use inside the loop, where the
-      // wait would also drain the K/V DMA in flight.
+      // The Q fragments are taken in right after an item's first K/V DMA is
+      // issued (take_q below): the wait the compiler puts there covers the Q
+      // loads and that DMA together.  Left to its first use inside a loop,
+      // the wait would also drain the DMA of the next step.
+      auto take_q = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) asm volatile("" :: "v"(qf[ks]));
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" :: "v"(qf[ks]));
+      };
       f32x16 acc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -661,6 +664,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           int ec = ldc(dl, k);
           int en = k >= 1 ? ldc(dl, k - 1) : -1;
           for (int u = -ec; u <= 3 - ec; ++u) issue_block(u);
+          take_q();
           StepWords wc = load_words(ec);
           int ep = -1;
           while (true) {
@@ -835,6 +839,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           issue_tile<false>(kbp, a.Nk, cur, s_cols, ring, w, l, off_k);
           issue_tile<true>(vbp, a.Nk, cur, s_cols, ring + TK * 256, w, l, off_v);
         }
+        take_q();
         // One tile step on ring stage `stage` (a compile-time constant, so every
         // LDS address below is a lane-constant register plus an immediate).
         auto step = [&](auto stage_c) {
