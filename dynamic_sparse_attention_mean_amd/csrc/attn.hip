@@ -70,6 +70,20 @@ struct BhList {
   int16_t bh[kMaxHeadTable];
 };
 
+// Reads of the small per-head tables held in the kernel arguments at a
+// wave-uniform index, as whole dwords: gfx9 has no sub-dword scalar loads, so
+// an int16 or int8 element read directly becomes a vector load.
+static_assert(offsetof(Sched, heads) % 4 == 0 && offsetof(AttnArgs, kind) % 4 == 0, "dword-aligned tables");
+typedef int32_t __attribute__((may_alias)) alias_i32_t;
+__device__ __forceinline__ int arg_i16(const int16_t* t, int i) {
+  const int32_t w = reinterpret_cast<const alias_i32_t*>(t)[i >> 1];
+  return (i & 1) ? (w >> 16) : (int)(int16_t)(w & 0xFFFF);
+}
+__device__ __forceinline__ int arg_i8(const int8_t* t, int i) {
+  const int32_t w = reinterpret_cast<const alias_i32_t*>(t)[i >> 2];
+  return (int)(int8_t)(w >> (8 * (i & 3)));
+}
+
 // ------------------------------------------------------------------ bitmaps
 __device__ __forceinline__ bool test_bit(const uint32_t* bm, int i) { return (bm[i >> 5] >> (i & 31)) & 1u; }
 
@@ -405,14 +419,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       __syncthreads();
       if (tid == 0) s_misc[0] = atomicAdd(&a.counters[g], 1);
       __syncthreads();
-      const int itn = s_misc[0];
+      // wave-uniform, so that the head and kind lookups below are scalar loads
+      // from the kernel arguments rather than a chain of vector loads
+      const int itn = __builtin_amdgcn_readfirstlane(s_misc[0]);
       if (itn >= nitems) break;
 
       Item it;
-      it.bh = sc.heads[sc.qstart[g] + itn % nh];
+      it.bh = arg_i16(sc.heads, sc.qstart[g] + itn % nh);
       const int b = it.bh / a.H, h = it.bh % a.H;
       it.kvh = h / rep;
-      it.kind = a.kind[h];
+      it.kind = arg_i8(a.kind, h);
       const int p = sc.T2 - 1 - itn / nh;
       const int r0 = p * 2 * TQ;
       it.P0 = r0 + a.q_offset;
