@@ -163,8 +163,11 @@ __global__ __launch_bounds__(NTI) void qk_heads_kernel(const QkArgs a) {
   // both already given a whole tile of compute to finish.  Buffer stores: lanes
   // with nothing to write get an offset past the end, which the hardware drops.
   const int nrow = MODE == MODE_ROUTER ? 0 : max(0, min(QPW, a.Nq - q0));
+  // bytes of this wave's score rows: at most 4 rows of 2^27 floats, 2^31 bytes, which
+  // fits the descriptor's unsigned 32-bit record count (computed without signed overflow)
+  const uint32_t obytes = (uint32_t)((size_t)nrow * (size_t)a.Nk * 4u);
   const __amdgpu_buffer_rsrc_t orow =
-      __builtin_amdgcn_make_buffer_rsrc(a.out + (size_t)min(q0, a.Nq) * a.Nk, (short)0, nrow * a.Nk * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(a.out + (size_t)min(q0, a.Nq) * a.Nk, (short)0, (int)obytes, 0x00020000);
   float pend_v[2][QPW];
   uint32_t pend_o[2][QPW];
 #pragma unroll
@@ -303,6 +306,8 @@ __global__ __launch_bounds__(TS_THREADS) void token_select_kernel(const float* s
 constexpr int CS_WAVES = 4;       // queries (waves) per workgroup
 
 // score[q, c] = sum_h w[q, h] max(0, q_idx[q, h] . k_idx[cand[q, c]]) for c < ccount[q].
+// Candidate rows have stride ccap (the caller's list capacity), score rows
+// stride ostride (the workspace's, which holds exactly `cand` per query).
 // One wave per query: rows 32 hb + m of the A operand are heads, columns the
 // 32 candidates of a block; the next block's keys are loaded while this one's
 // MFMAs run.
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_score_kernel(const uint16_
                                                                    const float* __restrict__ w,
                                                                    const int32_t* __restrict__ cand,
                                                                    const int32_t* __restrict__ ccount, int Nq, int Hi,
-                                                                   int ccap, float* __restrict__ out) {
+                                                                   int ccap, int ostride, float* __restrict__ out) {
   const int wv_ = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = blockIdx.x * CS_WAVES + wv_;
   if (q >= Nq) return;
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_score_kernel(const uint16_
   }
   const int n = __builtin_amdgcn_readfirstlane(ccount[q]);
   const int32_t* cq = cand + (size_t)q * ccap;
-  float* oq = out + (size_t)q * ccap;
+  float* oq = out + (size_t)q * ostride;
   const int nb = (n + 31) / 32;
   // this lane's key row of block b: candidate 32 b + qn (the first one past the end)
   auto load = [&](int b, u32x4 (&kf)[8]) {
@@ -373,14 +378,14 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_score_kernel(const uint16_
 
 // Top-k of a query's rescored candidates (ties to the lower position, which is
 // the lower key: candidate lists ascend), mapped back to key indices.
-__global__ __launch_bounds__(TS_THREADS) void cand_select_kernel(const float* scores, const int32_t* cand,
-                                                                 const int32_t* ccount, int ccap, int k, int32_t* tok,
-                                                                 int32_t* cnt, int cap) {
+__global__ __launch_bounds__(TS_THREADS) void cand_select_kernel(const float* scores, int sstride,
+                                                                 const int32_t* cand, const int32_t* ccount, int ccap,
+                                                                 int k, int32_t* tok, int32_t* cnt, int cap) {
   __shared__ Select3Smem<TS_THREADS> sm;
   __shared__ int32_t pos[kMaxTokensPerQuery];
   const int q = blockIdx.x;
   const int n = ccount[q];
-  const int m = select_topk_3pass<TS_THREADS>(scores + (size_t)q * ccap, n, min(k, kMaxTokensPerQuery), pos, sm);
+  const int m = select_topk_3pass<TS_THREADS>(scores + (size_t)q * sstride, n, min(k, kMaxTokensPerQuery), pos, sm);
   __syncthreads();
   for (int r = threadIdx.x; r < m; r += TS_THREADS) tok[(size_t)q * cap + r] = cand[(size_t)q * ccap + pos[r]];
   if (threadIdx.x == 0) cnt[q] = m;
@@ -424,9 +429,11 @@ __global__ __launch_bounds__(TA_THREADS) void token_attn_kernel(const uint16_t* 
   const int sub = l & 15, tg = l >> 4;
   const int n = min(min(tcount[(size_t)b * Nq + i], tcap), TA_MAXTOK);
   const int32_t* tl = tidx + ((size_t)b * Nq + i) * tcap;
+  // keys after the query's position (j > p_i) are not part of M(i): dropped like out-of-range ones
+  const int p_i = i + (Nk - Nq);
   for (int x = tid; x < n; x += TA_THREADS) {
     const int j = tl[x];
-    s_t[x] = (j >= 0 && j < Nk) ? j : -1;
+    s_t[x] = (j >= 0 && j <= p_i) ? j : -1;
   }
   __syncthreads();
   const uint16_t* qrow = q + (((size_t)b * H + h) * Nq + i) * 128;
@@ -577,9 +584,11 @@ __global__ __launch_bounds__(TG_WAVES * 64) void token_attn_group_kernel(
     u32x4 vx[8];
     bool kval[2];
   };
+  // keys after the query's position (j > p_i) are not part of M(i): dropped like out-of-range ones
+  const int p_i = i + (Nk - Nq);
   auto token = [&](int x, bool& ok) {
     int j = x < n ? tl[x] : -1;
-    ok = j >= 0 && j < Nk;
+    ok = j >= 0 && j <= p_i;
     return ok ? j : 0;
   };
   auto load = [&](int c0, Chunk& c) {
@@ -769,9 +778,9 @@ hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(token_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, scores, a.Nq, a.Nk, a.q_offset, a.cand,
                        cidx, ccnt, ccap);
     hipLaunchKernelGGL(cand_score_kernel, dim3((a.Nq + CS_WAVES - 1) / CS_WAVES), dim3(CS_WAVES * 64), 0, st, a.q_idx,
-                       a.k_idx, a.w, cidx, ccnt, a.Nq, a.Hi, ccap, resc);
-    hipLaunchKernelGGL(cand_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, resc, cidx, ccnt, ccap, a.topk, a.tok,
-                       a.tok_count, a.tok_cap);
+                       a.k_idx, a.w, cidx, ccnt, a.Nq, a.Hi, ccap, a.cand, resc);
+    hipLaunchKernelGGL(cand_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, resc, a.cand, cidx, ccnt, ccap, a.topk,
+                       a.tok, a.tok_count, a.tok_cap);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(token_select_kernel, dim3(a.Nq), dim3(TS_THREADS), 0, st, scores, a.Nq, a.Nk, a.q_offset, a.topk, a.tok,

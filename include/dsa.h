@@ -104,7 +104,9 @@ typedef struct dsa_block_index {
 } dsa_block_index;
 
 /* Token index set (device memory, caller-owned), one list per query shared by
- * all heads: idx[b][i][0 .. count[b][i]) are keys j <= p_i, ascending. */
+ * all heads: idx[b][i][0 .. count[b][i]) are keys j <= p_i, ascending.  The
+ * attention ignores entries outside [0, p_i] (negative, or after the query's
+ * own position): M(i) is causal whatever the list holds. */
 typedef struct dsa_token_index {
   int32_t* idx;          /* [B, Nq, cap] */
   int32_t* count;        /* [B, Nq] */

@@ -117,6 +117,29 @@ def vs_single(seed: int = 1, N: int = 4096, last_q: int = 64, nv: int = 256, ns:
     return Workload(f"vs_single_N{N}", q, k, v, plan, extra={"planted_cols": pos})
 
 
+def vs_multi(seed: int, B: int, H: int, Hkv: int, Nk: int, Nq: Optional[int] = None, last_q: int = 64,
+             n_plant: int = 4) -> Workload:
+    """Vertical-Slash inputs for several batches and heads, possibly a chunk
+    (Nq < Nk, the chunk ends at the last key).  Per (batch, KV head), `n_plant`
+    distinct key rows in [0, Nk - last_q) are set to 4 x the direction of the
+    mean of the group's last `last_q` queries."""
+    Nq = Nk if Nq is None else Nq
+    g = _gen(seed)
+    q, k, v = _qkv(g, B, H, Hkv, Nk, Nq=Nq)
+    qb = q.to(torch.bfloat16).float()
+    rep = H // Hkv
+    planted = []
+    for b in range(B):
+        for kvh in range(Hkv):
+            m = qb[b, kvh * rep:(kvh + 1) * rep, Nq - last_q:].reshape(-1, D).mean(0)
+            pos = _distinct(g, n_plant, 0, max(1, Nk - last_q))
+            k[b, kvh, pos] = 4.0 * m * (math.sqrt(D) / m.norm())
+            planted.append(pos)
+    q, k, v = _bf(q, k, v)
+    plan = [HeadPlan(VS, last_q=last_q) for _ in range(H)]
+    return Workload(f"vs_multi{seed}", q, k, v, plan, q_offset=Nk - Nq, extra={"planted_cols": planted})
+
+
 # ---------------------------------------------------------------------------
 # Workload 2: block-sparse heads, N = 32768, block 64.
 # ---------------------------------------------------------------------------

@@ -230,3 +230,60 @@ def test_token_attention_batch2(H, Hkv):
             ref_o, ref_l = O.attention_rows(f64(q[b, h]), f64(kk[b, h // rep]), f64(v[b, h // rep]), list(range(Nq)),
                                             tok[b])
             assert_attention_close(o[b, h].cpu().numpy(), lse[b, h].cpu().numpy(), ref_o, ref_l, f"b={b} head {h}")
+
+
+def test_hierarchical_candidate_capacity_above_cand():
+    """A caller candidate list wider than `cand` (cap = cand + 64): the results
+    equal those of cap == cand, and nothing is written past the workspace the
+    library asked for (a guard region after it keeps its fill pattern)."""
+    N, Nq, Hi, route, cand, topk = 1500, 90, 64, 8, 300, 64
+    w = small_chunk(21 + N, N, Nq, Hi, topk)
+    qi, ki, wt = (w.extra[x].to(DEV) for x in ("q_idx", "k_idx", "w"))
+    shape = dsa.Shape(1, 1, 1, Nq, N, 128, N - Nq)
+    need = dsa.workspace_size(dsa.OP_TOKENS_HIER, shape, [Hi, route, cand, topk])
+    guard = 1 << 20
+    results = []
+    for cap in (cand, cand + 64):
+        buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+        out = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+        cands = dsa.TokenIndex.empty(1, Nq, cap, DEV)
+        dsa.build_index_tokens_hier(qi, ki, wt, cand, topk, out, route_heads=route, cands=cands, ws=buf[:need])
+        torch.cuda.synchronize()
+        assert torch.all(buf[need:] == 0xA5), f"cap {cap}: workspace overrun"
+        results.append((out.idx.cpu(), out.count.cpu(), cands.idx[..., :cand].cpu(), cands.count.cpu()))
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
+
+
+def test_token_attention_ignores_noncausal_entries():
+    """Token lists that also hold keys after the query's position (and a
+    negative entry): those entries are not part of M(i), so the output equals
+    the oracle over the causal entries only (per-head and grouped kernels)."""
+    N, Nq, k = 700, 60, 80
+    for H, Hkv in ((4, 4), (16, 1)):
+        g = np.random.default_rng(300 + H)
+        q, kk, v = synth.random_qkv(310 + H, 1, H, Hkv, N, Nq=Nq)
+        qo = N - Nq
+        causal, lists = [], []
+        for i in range(Nq):
+            p = i + qo
+            c = np.sort(g.choice(p + 1, int(g.integers(1, k // 2)), replace=False))
+            extra = np.array([p + 1 + x for x in range(min(5, N - 1 - p))] + [-3], dtype=np.int64)
+            causal.append(c)
+            lists.append(np.sort(np.concatenate([c, extra])))
+        ti = dsa.TokenIndex.empty(1, Nq, k, DEV)
+        idx = torch.zeros(1, Nq, k, dtype=torch.int32)
+        cnt = torch.zeros(1, Nq, dtype=torch.int32)
+        for i, L in enumerate(lists):
+            idx[0, i, :len(L)] = torch.from_numpy(L.astype(np.int32))
+            cnt[0, i] = len(L)
+        ti.idx.copy_(idx)
+        ti.count.copy_(cnt)
+        o, lse = dsa.sparse_prefill_attn(q.to(DEV), kk.to(DEV), v.to(DEV), [dsa.TOKEN] * H, tok=ti)
+        torch.cuda.synchronize()
+        rep = H // Hkv
+        for h in range(H):
+            ref_o, ref_l = O.attention_rows(f64(q[0, h]), f64(kk[0, h // rep]), f64(v[0, h // rep]), list(range(Nq)),
+                                            causal)
+            assert_attention_close(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), ref_o, ref_l,
+                                   f"H={H} head {h}")

@@ -68,6 +68,83 @@ def test_block_index_parity(N, block, mode, force):
 # ---------------------------------------------------------------------------
 # Vertical-Slash: scores and sets
 # ---------------------------------------------------------------------------
+def assert_vs_scores_close(got, ref, last_q, what):
+    """Column / diagonal sums within 1e-5 of each value, relative, with an
+    absolute floor of 1e-7 of the mean value (last_q / N): sums far below the
+    mean sit far below any cutoff.  The fp32 scoring path carries ~1e-6
+    relative error (logits accumulated in fp32, exp2 to about an ulp)."""
+    tol = 1e-5 * np.abs(ref) + 1e-7 * last_q / len(ref)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} values off, worst rel "
+                           f"{(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)).max():.3g}")
+
+
+def check_vs_sets(out, b, h, v, s, nv, ns, what):
+    N = len(v)
+    for name, sc, kk, g, cnt in (("cols", v, nv, out.cols, out.cols_count), ("diags", s, ns, out.diags, out.diags_count)):
+        sel, c, tol = band_topk(sc, np.arange(N), kk, rel_only=True)
+        n = int(cnt[b, h].item())
+        assert_set_matches(g[b, h, :n].cpu().numpy(), sc, sel, c, tol, expect_count=min(kk, N), what=f"{what} {name}")
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nk,Nq,heads,last_q", [(2, 4, 2, 1000, 1000, [3, 0, 2], 64),
+                                                        (1, 4, 2, 1280, 320, [1, 2, 3], 64),
+                                                        (2, 2, 1, 900, 333, [1, 0], 33)])
+def test_vs_index_batch_and_chunk(B, H, Hkv, Nk, Nq, heads, last_q):
+    """build_index_vs with batch 2, heads listed out of order, and chunks that
+    end at the last key (q_offset = Nk - Nq > 0): the v / s rows (listed order)
+    and the index sets of every (batch, listed head) against the oracle."""
+    w = synth.vs_multi(seed=70 + Nk + Nq, B=B, H=H, Hkv=Hkv, Nk=Nk, Nq=Nq, last_q=last_q)
+    q, k, _ = dev(w)
+    nv, ns = 40, 90
+    out = dsa.VSIndex.empty(B, H, nv, ns, DEV)
+    vsc = torch.zeros(B, len(heads), Nk, device=DEV)
+    ssc = torch.zeros(B, len(heads), Nk, device=DEV)
+    dsa.build_index_vs(q, k, heads, last_q, nv, ns, out, v_scores=vsc, s_scores=ssc)
+    torch.cuda.synchronize()
+    listed = set(heads)
+    for b in range(B):
+        for t, h in enumerate(heads):
+            v, s = O.vs_scores(f64(w.q[b, h, Nq - last_q:]), f64(w.k[b, h // (H // Hkv)]))
+            assert_vs_scores_close(vsc[b, t].cpu().double().numpy(), v, last_q, f"b{b} h{h} v")
+            assert_vs_scores_close(ssc[b, t].cpu().double().numpy(), s, last_q, f"b{b} h{h} s")
+            check_vs_sets(out, b, h, v, s, nv, ns, f"b{b} h{h}")
+        for h in range(H):
+            if h not in listed:
+                assert int(out.cols_count[b, h]) == 0 and int(out.diags_count[b, h]) == 0, "unlisted head written"
+
+
+@pytest.mark.parametrize("block,mode", [(64, "topk"), (32, "thresh"), (128, "topk")])
+def test_block_index_batch2(block, mode):
+    """build_index_block with batch 2, GQA 4/2 and heads listed out of order:
+    pooled vectors bit-exact, scores and selections of every (batch, listed head)."""
+    N, B, H, Hkv = 1500, 2, 4, 2
+    w = synth.block_planted(seed=90 + block, B=B, H=H, Hkv=Hkv, N=N, block=block, n_plant=3, mode=mode, topk=4,
+                            force=mode == "topk")
+    q, k, _ = dev(w)
+    heads = [2, 0, 3]
+    nqb = -(-N // block)
+    cap = nqb if mode == "thresh" else min(nqb, 6)
+    out = dsa.BlockIndex.empty(B, H, nqb, cap, block, DEV)
+    qbar = torch.zeros(B, H, nqb, 128, dtype=torch.bfloat16, device=DEV)
+    kbar = torch.zeros(B, Hkv, nqb, 128, dtype=torch.bfloat16, device=DEV)
+    scores = torch.zeros(B, len(heads), nqb, nqb, dtype=torch.float32, device=DEV)
+    force = mode == "topk"
+    dsa.build_index_block(q, k, heads, block, dsa.TOPK if mode == "topk" else dsa.THRESHOLD, 4, out,
+                          force_first=force, force_diag=force, qbar=qbar, kbar=kbar, scores=scores)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for t, h in enumerate(heads):
+            _, sel, S, qb, kb = oracle_head_sets(w, b, h)
+            assert np.array_equal(f64(qbar[b, h].cpu()), qb), "pooled Q must be bit-exact"
+            assert np.array_equal(f64(kbar[b, h // 2].cpu()), kb), "pooled K must be bit-exact"
+            g = scores[b, t].cpu().double().numpy()
+            tri = np.tril(np.ones_like(S, dtype=bool))
+            assert np.all(np.isneginf(g[~tri]))
+            assert np.abs(g[tri] - S[tri]).max() <= 1e-5 * max(1.0, np.abs(S[tri]).max())
+            check_block_selection(out.idx[b, h].cpu().numpy(), out.count[b, h].cpu().numpy(), S, mode, 4,
+                                  -math.log(20.0), force, force, what=f"b{b} head {h}")
+        assert int(out.count[b, 1].sum()) == 0, "unlisted head written"
 @pytest.mark.parametrize("N,last_q,nv,ns", [(1000, 64, 64, 64), (2048, 17, 100, 300), (130, 64, 8, 8)])
 def test_vs_index_parity(N, last_q, nv, ns):
     w = synth.vs_single(seed=30 + N, N=N, last_q=last_q, nv=nv, ns=ns, n_plant=4)
@@ -80,7 +157,8 @@ def test_vs_index_parity(N, last_q, nv, ns):
     v, s = O.vs_scores(f64(w.q[0, 0, N - last_q:]), f64(w.k[0, 0]))
     gv = vsc[0, 0].cpu().double().numpy()
     gs = ssc[0, 0].cpu().double().numpy()
-    assert np.abs(gv - v).max() <= 1e-5 * last_q and np.abs(gs - s).max() <= 1e-5 * last_q
+    assert_vs_scores_close(gv, v, last_q, "v")
+    assert_vs_scores_close(gs, s, last_q, "s")
     assert abs(gv.sum() - last_q) < 1e-3 and abs(gs.sum() - last_q) < 1e-3
     for name, sc, kk, g, cnt in (("cols", v, nv, out.cols, out.cols_count), ("diags", s, ns, out.diags, out.diags_count)):
         sel, c, tol = band_topk(sc, np.arange(N), kk, rel_only=True)
