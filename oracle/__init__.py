@@ -21,7 +21,8 @@ per function, each citing the passage it follows.  Pages cited:
 Parity status: every function is pinned by a test in ``tests/test_oracle.py``
 against brute force, a closed form or a library routine, except the choices
 the pages leave open (router aggregation, forced blocks with the threshold
-rule, indexer key sharing, the two stages of the hierarchical indexer); those
+rule, indexer key sharing, the two stages of the hierarchical indexer, the
+rule that turns pooled block scores into vertical and slash sets); those
 are "parity unpinned" beyond brute force of the chosen definition, as stated
 in their docstrings.
 """
@@ -35,6 +36,7 @@ from .rules import (
 from .attention import masked_attention, attention_rows
 from .indexer import indexer_scores, router_heads, token_topk, indexer_row, hierarchical_tokens
 from .work import selected_count_vs, selected_count_block, selected_count_dense
+from .discovery import pooled_vs_scores, pooled_vs_blocks, expand_blocks, pooled_vs_sets
 
 __all__ = [
     "round_bf16", "to_f64",
@@ -45,4 +47,5 @@ __all__ = [
     "masked_attention", "attention_rows",
     "indexer_scores", "router_heads", "token_topk", "indexer_row", "hierarchical_tokens",
     "selected_count_vs", "selected_count_block", "selected_count_dense",
+    "pooled_vs_scores", "pooled_vs_blocks", "expand_blocks", "pooled_vs_sets",
 ]

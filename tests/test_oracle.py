@@ -472,6 +472,98 @@ def test_hierarchical_special_cases():
 # ---------------------------------------------------------------------------
 # Hand-written closed-form fixtures
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# Vertical and slash discovery from pooled block scores (reading O-22)
+# ---------------------------------------------------------------------------
+def _pooled_brute(S):
+    """Row softmax and its column / block-diagonal sums with explicit loops."""
+    nq, nk = S.shape
+    v = [0.0] * nk
+    s = [0.0] * nq
+    for I in range(nq):
+        m = max(S[I][J] for J in range(I + 1))
+        den = sum(math.exp(S[I][J] - m) for J in range(I + 1))
+        for J in range(I + 1):
+            p = math.exp(S[I][J] - m) / den
+            v[J] += p
+            s[I - J] += p
+    return np.array(v), np.array(s)
+
+
+@pytest.mark.parametrize("nq", [1, 2, 7, 33])
+def test_pooled_vs_scores_brute_force(nq):
+    S = RNG.standard_normal((nq, nq)) * 3.0
+    S = np.where(np.tril(np.ones((nq, nq), dtype=bool)), S, -np.inf)
+    v, s = O.pooled_vs_scores(S)
+    vb, sb = _pooled_brute(S)
+    assert np.allclose(v, vb, rtol=1e-12, atol=1e-14) and np.allclose(s, sb, rtol=1e-12, atol=1e-14)
+    # every row's weights sum to one: both masses total the number of query blocks
+    assert abs(v.sum() - nq) < 1e-12 and abs(s.sum() - nq) < 1e-12
+    assert np.all(v >= 0) and np.all(s >= 0) and v.max() <= nq and s.max() <= nq
+
+
+def test_pooled_vs_scores_equal_scores_harmonic():
+    """Equal scores give P[I, J] = 1 / (I + 1), so vbar[J] = H(n) - H(J) and
+    sbar[D] = H(n) - H(D) with H the harmonic numbers (exact fractions)."""
+    n = 12
+    S = np.where(np.tril(np.ones((n, n), dtype=bool)), 0.0, -np.inf)
+    v, s = O.pooled_vs_scores(S)
+    H = [sum((Fraction(1, m) for m in range(1, t + 1)), Fraction(0)) for t in range(n + 1)]
+    want = np.array([float(H[n] - H[j]) for j in range(n)])
+    assert np.allclose(v, want, rtol=1e-13) and np.allclose(s, want, rtol=1e-13)
+    # strictly decreasing: the top-k are the first k indices
+    Vb, Sb = O.pooled_vs_blocks(v, s, 3, 5)
+    assert Vb.tolist() == [0, 1, 2] and Sb.tolist() == [0, 1, 2, 3, 4]
+
+
+def test_pooled_vs_single_token_blocks_are_vertical_slash_of_every_row():
+    """With blocks of one token the pooled vectors are the rows themselves, and
+    vbar / sbar are the Vertical-Slash column and diagonal sums taken over every
+    query row (last_q = N)."""
+    N, d = 40, 8
+    q, k = bf16_array((N, d)), bf16_array((N, d))
+    S = O.block_scores(O.block_means(q, 1), O.block_means(k, 1))
+    v, s = O.pooled_vs_scores(S)
+    v2, s2 = O.vs_scores(q, k)
+    assert np.allclose(v, v2, rtol=1e-12, atol=1e-15) and np.allclose(s, s2, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("N,block", [(37, 4), (64, 8), (50, 16), (9, 1)])
+def test_expand_blocks_brute_force(N, block):
+    """Token columns and diagonals of kept blocks against enumeration of every
+    pair j <= i < N."""
+    nb = -(-N // block)
+    rng = np.random.default_rng(N + block)
+    Vb = np.sort(rng.choice(nb, min(nb, 3), replace=False))
+    Sb = np.sort(rng.choice(nb, min(nb, 3), replace=False))
+    cols, diags = O.expand_blocks(Vb, Sb, block, N)
+    assert cols.tolist() == [j for j in range(N) if j // block in set(Vb.tolist())]
+    want = sorted({i - j for i in range(N) for j in range(i + 1) if (i // block - j // block) in set(Sb.tolist())})
+    assert diags.tolist() == want
+
+
+def test_pooled_vs_sets_find_planted_structure():
+    """A key block made to match every query is the top vertical block; query
+    and key blocks that share a direction whenever they lie 3 blocks apart make
+    block offset 3 the top slash offset, expanded to token offsets 3B - (B - 1)
+    .. 3B + (B - 1)."""
+    N, d, B = 512, 16, 32
+    nb = N // B
+    rng = np.random.default_rng(9)
+    u = rng.standard_normal(d)
+    dirs = rng.standard_normal((4, d)) * 2.0
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d))
+    for I in range(nb):
+        q[I * B:(I + 1) * B] += u + dirs[I % 4]
+        k[I * B:(I + 1) * B] += dirs[(I + 3) % 4]
+    k[5 * B:6 * B] += 4.0 * u
+    q, k = O.round_bf16(q), O.round_bf16(k)
+    cols, diags, v, s, Vb, Sb = O.pooled_vs_sets(q, k, B, 1, 1)
+    assert Vb.tolist() == [5] and cols.tolist() == list(range(5 * B, 6 * B))
+    assert Sb.tolist() == [3] and diags.tolist() == list(range(3 * B - (B - 1), 3 * B + B))
+
+
 def test_golden_closed_forms():
     with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
         cases = json.load(f)["cases"]
