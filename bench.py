@@ -48,6 +48,9 @@ WORKLOADS = {
     "mixed128k": ("mixed-pattern layer, 32 Q / 8 KV heads, d=128, N=131072: heads 0-10 A-shape (sink 128, local "
                   "2048), 11-26 Vertical-Slash (last_q 64, 1000 cols, 4096 diags), 27-31 block top-128 of 64",
                   lambda: synth.config(3)),
+    "mixed128k-pooled": ("mixed-pattern layer as mixed128k, with the Vertical-Slash heads 11-26 discovered from "
+                         "pooled block scores (block 64: 16 key blocks, 32 block offsets)",
+                         lambda: synth.config(3, vs_rule="pooled")),
     "vs4k": ("one Vertical-Slash head, N=4096, last_q 64, 256 cols + 256 diags", lambda: synth.config(1)),
     "block32k-topk": ("8 block heads, N=32768, block 64, top-16 + first + diagonal", lambda: synth.config(2)),
     "block32k-thresh": ("8 block heads, N=32768, block 64, threshold max - ln 20 + first + diagonal",
@@ -337,6 +340,68 @@ def block_sweep(args, dev, stream):
     print(json.dumps(rec), flush=True)
 
 
+def vs_compare(args, dev, stream):
+    """Vertical-Slash discovery on the 128K mixed layer's data: last_q scoring
+    against pooled block scores, for the 16 Vertical-Slash heads.  For each
+    rule: time of its index build (those heads only) and of the whole layer,
+    recall of the planted vertical keys (the heads' KV group's 64 planted rows),
+    the attention mass the sets keep (the dense softmax weight of the selected
+    keys, exp(LSE_sparse - LSE_dense), averaged over every row of the heads),
+    and the heads' attention output against dense causal attention (mean and
+    max abs difference over every row).  One JSON line."""
+    w = synth.config(3)
+    B, H, Hkv, Nq, Nk, d = w.shape
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    vs_heads = [h for h, p in enumerate(w.heads) if p.kind == dsa.VS and not p.ashape]
+    # dense causal reference (every head; only the Vertical-Slash heads are compared)
+    dense_o = torch.empty(B, H, Nq, d, dtype=torch.float32, device=dev)
+    dense_lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
+    dws = torch.empty(dsa.workspace_size(dsa.OP_ATTN, dsa.make_shape(q, k)), dtype=torch.uint8, device=dev)
+    dsa.sparse_prefill_attn(q, k, v, [dsa.DENSE] * H, out_dtype=dsa.OUT_F32, o=dense_o, lse=dense_lse, ws=dws)
+    torch.cuda.synchronize()
+    del dws
+    out = {}
+    for rule in ("last_q", "pooled"):
+        pooled_plan = synth.HeadPlan(dsa.VS, pooled=True, block=64, nv_blocks=16, ns_blocks=32)
+        plan = [pooled_plan if (rule == "pooled" and h in vs_heads) else w.heads[h] for h in range(H)]
+        wr = synth.Workload(w.name, w.q, w.k, w.v, plan, w.q_offset, w.extra)
+        layer = SparsePrefillLayer(plan, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_F32, want_lse=True)
+        vsi = layer.vs_index
+        if rule == "pooled":
+            (blk, nvb, nsb), hs = next(iter(layer.pooled.items()))
+            build_vs = lambda: dsa.build_index_vs_pooled(q, k, hs, blk, nvb, nsb, vsi, ws=layer.ws)
+        else:
+            (lq, nv, ns), hs = next(iter(layer.vs.items()))
+            build_vs = lambda: dsa.build_index_vs(q, k, hs, lq, nv, ns, vsi, ws=layer.ws)
+        ms_vs, _, _ = time_steps([build_vs], args.steps, args.warmup, stream)
+        phases = [lambda: layer.build_indices(q, k), lambda: layer.attention(q, k, v)]
+        ms_step, (ms_index, ms_attn), _ = time_steps(phases, args.steps, args.warmup, stream)
+        rv = 0.0
+        for h in vs_heads:
+            cols = vsi.cols[0, h, :int(vsi.cols_count[0, h])].cpu().numpy()
+            rv += np.isin(w.extra["planted_cols"][h // (H // Hkv)].numpy(), cols).mean()
+        mass = torch.exp(layer.lse[0, vs_heads].double() - dense_lse[0, vs_heads].double())
+        diff = (layer.o[0, vs_heads] - dense_o[0, vs_heads]).abs()
+        f_sel = 4 * d * selected_count_layer(layer, wr)
+        out[rule] = {"ms_vs_index": round(ms_vs, 4), "ms_index": round(ms_index, 4), "ms_attn": round(ms_attn, 4),
+                     "ms_step": round(ms_step, 4), "effective_tflops": round(f_sel / (ms_step * 1e-3) / 1e12, 2),
+                     "recall_vertical": round(rv / len(vs_heads), 4),
+                     "attention_mass_kept": round(float(mass.mean()), 4),
+                     "attention_mass_kept_min_row": round(float(mass.min()), 4),
+                     "vs_heads_vs_dense_mean_abs": round(float(diff.mean()), 5),
+                     "vs_heads_vs_dense_max_abs": round(float(diff.max()), 4)}
+        log(f"[bench] {rule}: {out[rule]}")
+        del layer
+        torch.cuda.synchronize()
+    rec = {"metric": "Vertical-Slash discovery on the 128K mixed layer: last_q scoring vs pooled block scores",
+           "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": WORKLOADS["mixed128k"][0], "name": "vscompare128k", "vs_heads": vs_heads,
+                      "pooled": "block 64, 16 key blocks (1024 columns), 32 block offsets (<= 4064 diagonals)",
+                      "rules": out}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +413,9 @@ def main():
                     help="skip the cold-cache steps (profiling runs: every launch is then a warm one)")
     ap.add_argument("--block-sweep", action="store_true",
                     help="only run the block-size sweep (recall of planted keys, time per block size) and exit")
+    ap.add_argument("--vs-compare", action="store_true",
+                    help="only compare Vertical-Slash discovery by last_q scoring and by pooled block scores on the "
+                         "128K mixed layer (time, recall, output against dense) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -361,6 +429,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.block_sweep:
         block_sweep(args, dev, torch.cuda.current_stream(dev))
+        return
+    if args.vs_compare:
+        vs_compare(args, dev, torch.cuda.current_stream(dev))
         return
     desc, make = WORKLOADS[args.workload]
     log(f"[bench] generating {args.workload}")

@@ -23,11 +23,11 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 DENSE, VS, BLOCK, TOKEN = 0, 1, 2, 3
 TOPK, THRESHOLD = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
-OP_VS, OP_BLOCK, OP_TOKENS, OP_ATTN, OP_TOKENS_HIER = 1, 2, 3, 4, 5
+OP_VS, OP_BLOCK, OP_TOKENS, OP_ATTN, OP_TOKENS_HIER, OP_VS_POOLED = 1, 2, 3, 4, 5, 6
 
 EXPORTS = (
     "dsa_status_string", "dsa_last_error", "dsa_workspace_size", "build_index_ashape",
-    "build_index_vs", "build_index_block", "build_index_tokens", "build_index_tokens_hier", "sparse_prefill_attn",
+    "build_index_vs", "build_index_vs_pooled", "build_index_block", "build_index_tokens", "build_index_tokens_hier", "sparse_prefill_attn",
 )
 
 
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.build_index_ashape.argtypes = [ctypes.POINTER(Shape), P, I32, I32, I32, _VsIndexC, P]
         L.build_index_vs.restype = I32
         L.build_index_vs.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, _VsIndexC, P, P, P, SZ, P]
+        L.build_index_vs_pooled.restype = I32
+        L.build_index_vs_pooled.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, _VsIndexC, P, P, P,
+                                            SZ, P]
         L.build_index_block.restype = I32
         L.build_index_block.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, ctypes.c_float, I32, I32,
                                         _BlockIndexC, P, P, P, P, SZ, P]
@@ -217,6 +220,22 @@ def build_index_vs(q, k, heads, last_q, nv, ns, out: VSIndex, v_scores=None, s_s
     return out
 
 
+def build_index_vs_pooled(q, k, heads, block, nv_blocks, ns_blocks, out: VSIndex, v_scores=None, s_scores=None,
+                          ws=None):
+    """Vertical-Slash sets from the pooled block scores (the library's rule for
+    discovering vertical and slash shapes from one block search)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    shape = make_shape(q, k)
+    arr, n = _heads_arr(heads)
+    ws = _workspace(OP_VS_POOLED, shape, [n, block], q.device, ws)
+    _check(lib().build_index_vs_pooled(ctypes.byref(shape), _ptr(q), _ptr(k), arr, n, block, nv_blocks, ns_blocks,
+                                       out.c(), _ptr(v_scores), _ptr(s_scores), _ptr(ws), ws.numel(),
+                                       _stream(q.device)),
+           "build_index_vs_pooled")
+    return out
+
+
 def build_index_block(q, k, heads, block, mode, topk, out: BlockIndex, log_alpha=-math.log(20.0),
                       force_first=False, force_diag=False, qbar=None, kbar=None, scores=None, ws=None):
     _need(q, "q", torch.bfloat16)
@@ -287,3 +306,4 @@ def sparse_prefill_attn(q, k, v, head_kind, vs: Optional[VSIndex] = None, blk: O
                                      out_dtype, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)),
            "sparse_prefill_attn")
     return o, lse
+

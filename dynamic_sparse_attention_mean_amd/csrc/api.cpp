@@ -89,12 +89,26 @@ size_t ws_vs(const dsa_shape* s, int n_heads) {
   return align256(vs_workspace_floats(s->batch * n_heads, s->kv_len) * 4) + 256;
 }
 
+// Pooled Q and K; the block scores stay on chip (a strip of query blocks per
+// workgroup) unless a row of them is too long for that, then they go through
+// the workspace.
 size_t ws_block(const dsa_shape* s, int n_heads, int block) {
   const size_t nqb = (s->q_len + block - 1) / block, nkb = (s->kv_len + block - 1) / block;
   WsCarver c(nullptr);
   c.take<uint16_t>((size_t)s->batch * s->heads * nqb * 128);
   c.take<uint16_t>((size_t)s->batch * s->kv_heads * nkb * 128);
-  c.take<float>((size_t)s->batch * n_heads * nqb * nkb);
+  if (block_strip_rows((int)nkb, nullptr) < 1) c.take<float>((size_t)s->batch * n_heads * nqb * nkb);
+  return c.off + 256;
+}
+
+// Pooled Q and K, the per-strip partial masses, and vbar / sbar.
+size_t ws_vs_pooled(const dsa_shape* s, int n_heads, int block) {
+  const size_t nqb = (s->q_len + block - 1) / block, nkb = (s->kv_len + block - 1) / block;
+  WsCarver c(nullptr);
+  c.take<uint16_t>((size_t)s->batch * s->heads * nqb * 128);
+  c.take<uint16_t>((size_t)s->batch * s->kv_heads * nkb * 128);
+  c.take<float>((size_t)s->batch * n_heads * pooled_vs_partial_floats((int)nqb, (int)nkb));
+  c.take<float>((size_t)s->batch * n_heads * (nqb + nkb));
   return c.off + 256;
 }
 
@@ -148,6 +162,11 @@ dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t*
       return DSA_OK;
     case DSA_OP_ATTN:
       *bytes = ws_attn(shape);
+      return DSA_OK;
+    case DSA_OP_VS_POOLED:
+      if (!need(2) || params[0] < 1 || params[0] > shape->heads || !block_size_ok(params[1]))
+        return fail(DSA_ERR_INVALID_ARG, "VS_POOLED params");
+      *bytes = ws_vs_pooled(shape, params[0], params[1]);
       return DSA_OK;
     default:
       return fail(DSA_ERR_INVALID_ARG, "unknown op %d", op);
@@ -240,10 +259,11 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
   const size_t need = ws_block(shape, n_heads, block);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
 
+  const bool on_chip = block_strip_rows(nkb, nullptr) >= 1;
   WsCarver c(ws);
   uint16_t* qb = c.take<uint16_t>((size_t)shape->batch * shape->heads * nqb * 128);
   uint16_t* kb = c.take<uint16_t>((size_t)shape->batch * shape->kv_heads * nkb * 128);
-  float* sc = c.take<float>((size_t)shape->batch * n_heads * nqb * nkb);
+  float* sc = on_chip ? nullptr : c.take<float>((size_t)shape->batch * n_heads * nqb * nkb);
   if (qbar) qb = (uint16_t*)qbar;
   if (kbar) kb = (uint16_t*)kbar;
   if (scores) sc = scores;
@@ -262,13 +282,81 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
   if ((st = hip_status(launch_pool((const uint16_t*)k, shape->batch, shape->kv_heads, shape->kv_len, kvl, block, kb, s),
                        "build_index_block: pool k")))
     return st;
-  if ((st = hip_status(launch_block_scores(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, hl,
-                                           (float)(1.0 / std::sqrt(128.0)), sc, s),
+  const float scale = (float)(1.0 / std::sqrt(128.0));
+  if (on_chip)
+    return hip_status(launch_block_index(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, hl, scale, mode,
+                                         topk, log_alpha, force_first, force_diag, out.idx, out.count, out.cap,
+                                         scores, s),
+                      "build_index_block: scores + select");
+  if ((st = hip_status(launch_block_scores(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, hl, scale,
+                                           sc, s),
                        "build_index_block: scores")))
     return st;
   return hip_status(launch_block_select(sc, shape->batch, shape->heads, nqb, nkb, hl, mode, topk, log_alpha,
                                         force_first, force_diag, out.idx, out.count, out.cap, s),
                     "build_index_block: select");
+}
+
+dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const void* k, const int32_t* heads,
+                                 int32_t n_heads, int32_t block, int32_t nv_blocks, int32_t ns_blocks,
+                                 dsa_vs_index out, float* v_scores, float* s_scores, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  g_err.clear();
+  dsa_status st = check_shape(shape);
+  if (st) return st;
+  HeadList hl;
+  if ((st = check_heads(shape, heads, n_heads, hl))) return st;
+  if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (!block_size_ok(block)) return fail(DSA_ERR_UNSUPPORTED, "block %d (16, 32, 64 or 128)", block);
+  if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "pooled discovery needs q_offset == 0");
+  if (nv_blocks < 0 || ns_blocks < 0 || nv_blocks > kMaxPooledBlocks || ns_blocks > kMaxPooledBlocks)
+    return fail(DSA_ERR_UNSUPPORTED, "nv_blocks and ns_blocks must be in [0, %d]", kMaxPooledBlocks);
+  const int nqb = (shape->q_len + block - 1) / block, nkb = (shape->kv_len + block - 1) / block;
+  if (block_strip_rows(nkb, nullptr) < 1)
+    return fail(DSA_ERR_UNSUPPORTED, "%d key blocks: a row of block scores does not fit on chip", nkb);
+  if (!out.cols || !out.cols_count || !out.diags || !out.diags_count)
+    return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
+  const int64_t need_c = std::min<int64_t>(shape->kv_len, (int64_t)nv_blocks * block);
+  const int64_t need_d = std::min<int64_t>(shape->kv_len, (int64_t)ns_blocks * (2 * block - 1));
+  if (out.cols_cap < need_c || out.diags_cap < need_d)
+    return fail(DSA_ERR_INVALID_ARG, "index set capacity too small (need %lld columns, %lld diagonals)",
+                (long long)need_c, (long long)need_d);
+  const size_t need = ws_vs_pooled(shape, n_heads, block);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+
+  const size_t R = (size_t)shape->batch * n_heads;
+  WsCarver c(ws);
+  uint16_t* qb = c.take<uint16_t>((size_t)shape->batch * shape->heads * nqb * 128);
+  uint16_t* kb = c.take<uint16_t>((size_t)shape->batch * shape->kv_heads * nkb * 128);
+  const size_t pf = pooled_vs_partial_floats(nqb, nkb);
+  float* part = c.take<float>(R * pf);
+  float* masses = c.take<float>(R * (nqb + nkb));
+  const int nstrips = (int)(pf / (size_t)(nqb + nkb));
+  float* vpart = part;
+  float* spart = part + R * (size_t)nstrips * nkb;
+  float* vbar = v_scores ? v_scores : masses;
+  float* sbar = s_scores ? s_scores : masses + R * nkb;
+  HeadList kvl;
+  kvl.n = 0;
+  bool kvseen[256] = {};
+  const int rep = shape->heads / shape->kv_heads;
+  for (int i = 0; i < hl.n; ++i) {
+    const int kvh = hl.h[i] / rep;
+    if (!kvseen[kvh]) { kvseen[kvh] = true; kvl.h[kvl.n++] = kvh; }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(launch_pool((const uint16_t*)q, shape->batch, shape->heads, shape->q_len, hl, block, qb, s),
+                       "build_index_vs_pooled: pool q")))
+    return st;
+  if ((st = hip_status(launch_pool((const uint16_t*)k, shape->batch, shape->kv_heads, shape->kv_len, kvl, block, kb, s),
+                       "build_index_vs_pooled: pool k")))
+    return st;
+  return hip_status(launch_pooled_vs(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, shape->kv_len,
+                                     block, hl, (float)(1.0 / std::sqrt(128.0)), vpart, spart, vbar, sbar, nv_blocks,
+                                     ns_blocks, out.cols, out.cols_count, out.cols_cap, out.diags, out.diags_count,
+                                     out.diags_cap, s),
+                    "build_index_vs_pooled");
 }
 
 dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const void* k_idx, const float* w,

@@ -31,8 +31,33 @@ hipError_t launch_block_scores(const uint16_t* qbar, const uint16_t* kbar, int B
                                int nqb, int nkb, const HeadList& heads, float scale, float* scores,
                                hipStream_t st);
 
+// --------------------------------------------- fused block scores + select
+// Scores of a strip of query blocks held on chip (LDS), then the selection of
+// every row of the strip; `scores` (nullable, [B, n_heads, nqb, nkb]) receives
+// an inspection copy.  block_strip_rows() gives the rows per strip for nkb key
+// blocks (0: a row does not fit on chip; the two-kernel path below then runs).
+constexpr int kBlockStripFloats = 32768;   // 128 KB of fp32 scores per workgroup
+int block_strip_rows(int nkb, int* stride);
+hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
+                              const HeadList& heads, float scale, int mode, int topk, float log_alpha,
+                              int force_first, int force_diag, int32_t* idx, int32_t* count, int cap,
+                              float* scores, hipStream_t st);
+
+// Vertical and slash discovery from the pooled block scores: per listed head,
+// the per-strip partials (vpart [B, n_heads, nstrips, nkb], spart [.., nqb];
+// pooled_vs_partial_floats() per row of B * n_heads), the masses vbar
+// [B, n_heads, nkb] and sbar [B, n_heads, nqb], the top nvb key blocks and nsb
+// block offsets, expanded into the Vertical-Slash set ([B, H, cap] rows).
+constexpr int kMaxPooledBlocks = 1024;     // kept key blocks / block offsets per head
+size_t pooled_vs_partial_floats(int nqb, int nkb);
+hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
+                            int Nk, int block, const HeadList& heads, float scale, float* vpart, float* spart,
+                            float* vbar, float* sbar, int nvb, int nsb, int32_t* cols, int32_t* cols_count,
+                            int cols_cap, int32_t* diags, int32_t* diags_count, int diags_cap, hipStream_t st);
+
 // ---------------------------------------------------------------- select
-// Per listed head and query block I: block selection over scores row I.
+// Per listed head and query block I: block selection over scores row I
+// (rows too long to keep on chip: the scores go through the workspace).
 hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb,
                                const HeadList& heads, int mode, int topk, float log_alpha,
                                int force_first, int force_diag, int32_t* idx, int32_t* count,

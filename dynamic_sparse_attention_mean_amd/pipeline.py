@@ -4,10 +4,11 @@ The per-head pattern table is the product of the method's offline search
 ("MInference 1.0" explainer, offline per-head pattern search; authors' abstract):
 here it is an input, a list with one entry per Q head carrying the fields
 
-  kind   : 1 (Vertical-Slash, with ashape=True for an A-shape head) or 2 (block)
-           or 0 (dense causal)
+  kind   : 1 (Vertical-Slash, with ashape=True for an A-shape head, pooled=True
+           for sets discovered from pooled block scores) or 2 (block) or 0 (dense)
   sink, local              (A-shape)
   last_q, nv, ns           (Vertical-Slash)
+  block, nv_blocks, ns_blocks  (Vertical-Slash from pooled block scores)
   block, mode, topk, log_alpha, force_first, force_diag   (block rule)
 
 All buffers (index sets, workspaces, outputs) are allocated once in the
@@ -20,9 +21,9 @@ from collections import OrderedDict
 
 import torch
 
-from . import (BLOCK, DENSE, OUT_F32, OP_ATTN, OP_BLOCK, OP_VS, THRESHOLD, TOPK, VS, BlockIndex, VSIndex,
-               build_index_ashape, build_index_block, build_index_vs, make_shape, sparse_prefill_attn,
-               workspace_size)
+from . import (BLOCK, DENSE, OUT_F32, OP_ATTN, OP_BLOCK, OP_VS, OP_VS_POOLED, THRESHOLD, TOPK, VS, BlockIndex,
+               VSIndex, build_index_ashape, build_index_block, build_index_vs, build_index_vs_pooled, make_shape,
+               sparse_prefill_attn, workspace_size)
 
 
 class SparsePrefillLayer:
@@ -34,10 +35,13 @@ class SparsePrefillLayer:
         self.kinds = [int(p.kind) for p in plan]
         self.ashape = OrderedDict()   # (sink, local) -> heads
         self.vs = OrderedDict()       # (last_q, nv, ns) -> heads
+        self.pooled = OrderedDict()   # (block, nv_blocks, ns_blocks) -> heads
         self.blk = OrderedDict()      # (block, mode, topk, log_alpha, ff, fd) -> heads
         for h, p in enumerate(plan):
             if p.kind == VS and getattr(p, "ashape", False):
                 self.ashape.setdefault((p.sink, p.local), []).append(h)
+            elif p.kind == VS and getattr(p, "pooled", False):
+                self.pooled.setdefault((p.block, p.nv_blocks, p.ns_blocks), []).append(h)
             elif p.kind == VS:
                 self.vs.setdefault((p.last_q, p.nv, p.ns), []).append(h)
             elif p.kind == BLOCK:
@@ -51,9 +55,12 @@ class SparsePrefillLayer:
             raise ValueError("one block size per layer")
         shape = make_shape(torch.empty(B, H, N, 128, device="meta"), torch.empty(B, Hkv, N, 128, device="meta"))
         self.shape = shape
-        cols_cap = max([min(s, N) for s, _ in self.ashape] + [nv for _, nv, _ in self.vs] + [1])
-        diags_cap = max([min(l, N) for _, l in self.ashape] + [ns for _, _, ns in self.vs] + [1])
-        self.vs_index = VSIndex.empty(B, H, cols_cap, diags_cap, device) if (self.ashape or self.vs) else None
+        cols_cap = max([min(s, N) for s, _ in self.ashape] + [nv for _, nv, _ in self.vs] +
+                       [min(N, b * nvb) for b, nvb, _ in self.pooled] + [1])
+        diags_cap = max([min(l, N) for _, l in self.ashape] + [ns for _, _, ns in self.vs] +
+                        [min(N, (2 * b - 1) * nsb) for b, _, nsb in self.pooled] + [1])
+        have_vs = bool(self.ashape or self.vs or self.pooled)
+        self.vs_index = VSIndex.empty(B, H, cols_cap, diags_cap, device) if have_vs else None
         self.blk_index = None
         if self.blk:
             block = blocks.pop()
@@ -67,6 +74,8 @@ class SparsePrefillLayer:
             ws = max(ws, workspace_size(OP_VS, shape, [len(hs), lq]))
         for key, hs in self.blk.items():
             ws = max(ws, workspace_size(OP_BLOCK, shape, [len(hs), key[0]]))
+        for (blk, _, _), hs in self.pooled.items():
+            ws = max(ws, workspace_size(OP_VS_POOLED, shape, [len(hs), blk]))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
         odt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
         self.o = torch.empty(B, H, N, 128, dtype=odt, device=device)
@@ -77,6 +86,8 @@ class SparsePrefillLayer:
             build_index_ashape(q, k, hs, sink, local, self.vs_index)
         for (lq, nv, ns), hs in self.vs.items():
             build_index_vs(q, k, hs, lq, nv, ns, self.vs_index, ws=self.ws)
+        for (blk, nvb, nsb), hs in self.pooled.items():
+            build_index_vs_pooled(q, k, hs, blk, nvb, nsb, self.vs_index, ws=self.ws)
         for (block, mode, topk, la, ff, fd), hs in self.blk.items():
             build_index_block(q, k, hs, block, mode, topk, self.blk_index, log_alpha=la, force_first=ff,
                               force_diag=fd, ws=self.ws)

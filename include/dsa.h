@@ -67,7 +67,8 @@ enum {
 
 enum { DSA_SELECT_TOPK = 0, DSA_SELECT_THRESHOLD = 1 };
 enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
-enum { DSA_OP_VS = 1, DSA_OP_BLOCK = 2, DSA_OP_TOKENS = 3, DSA_OP_ATTN = 4, DSA_OP_TOKENS_HIER = 5 };
+enum { DSA_OP_VS = 1, DSA_OP_BLOCK = 2, DSA_OP_TOKENS = 3, DSA_OP_ATTN = 4, DSA_OP_TOKENS_HIER = 5,
+       DSA_OP_VS_POOLED = 6 };
 
 typedef struct dsa_shape {
   int32_t batch;       /* B  >= 1 */
@@ -125,6 +126,7 @@ const char* dsa_last_error(void);
  *   DSA_OP_TOKENS: {n_idx_heads, route_heads, topk}
  *   DSA_OP_TOKENS_HIER: {n_idx_heads, route_heads, cand, topk}
  *   DSA_OP_ATTN:   {} (none)
+ *   DSA_OP_VS_POOLED: {n_heads, block}
  * Writes the size to *bytes.  Sizes depend on shapes only, never on data. */
 dsa_status dsa_workspace_size(int32_t op, const dsa_shape* shape, const int32_t* params,
                               int32_t n_params, size_t* bytes);
@@ -177,6 +179,31 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
                              int32_t force_first, int32_t force_diag,
                              dsa_block_index out, void* qbar, void* kbar, float* scores,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Vertical-Slash sets discovered from pooled block scores ("FlashPrefill"
+ * section 2.1: one search over blocks, keys represented by their block means,
+ * finds the vertical, slash and block shapes at once; the page states no rule
+ * for the first two, this is the one the library defines).  For each listed head:
+ *   Qbar, Kbar, S[I, J] = Qbar_I . Kbar_J / sqrt(d) (J <= I) as in
+ *   build_index_block; P[I, :] = softmax over J <= I of S[I, J];
+ *   vbar[J] = sum_I P[I, J] (vertical mass of key block J),
+ *   sbar[D] = sum_I P[I, I - D] (slash mass of block offset D);
+ *   kept key blocks = top-nv_blocks of vbar, kept offsets = top-ns_blocks of
+ *   sbar (ties to the lower index);
+ *   cols = every key of a kept key block, diags = every token offset
+ *   [max(0, D*block - (block-1)), min(Nk-1, D*block + (block-1))] of a kept D.
+ * The result goes to `out` like build_index_vs (attention takes it as a
+ * Vertical-Slash set).  block in {16, 32, 64, 128}; q_offset must be 0;
+ * 0 <= nv_blocks, ns_blocks <= 1024; cols_cap >= min(Nk, nv_blocks * block),
+ * diags_cap >= min(Nk, ns_blocks * (2 * block - 1)); at most 32768 key blocks.
+ * v_scores ([B, n_heads, nkb]) and s_scores ([B, n_heads, nqb]), nullable
+ * device floats, receive vbar and sbar in listed order.  Workspace:
+ * dsa_workspace_size(DSA_OP_VS_POOLED, {n_heads, block}). */
+dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const void* k,
+                                 const int32_t* heads, int32_t n_heads, int32_t block,
+                                 int32_t nv_blocks, int32_t ns_blocks, dsa_vs_index out,
+                                 float* v_scores, float* s_scores,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Indexer token top-k ("MISA": the DSA indexer scores every key with 64 light
  * heads and keeps the best tokens; MISA's router looks at keys in large blocks

@@ -62,6 +62,9 @@ class HeadPlan:
     nv: int = 0            # Vertical-Slash: columns kept
     ns: int = 0            # Vertical-Slash: diagonals kept
     ashape: bool = False   # A-shape heads are VS heads with closed-form sets
+    pooled: bool = False   # VS heads whose sets come from pooled block scores
+    nv_blocks: int = 0     # pooled discovery: key blocks kept
+    ns_blocks: int = 0     # pooled discovery: block offsets kept
     block: int = 0         # Block rule: block size
     mode: str = ""         # Block rule: "topk" or "thresh"
     topk: int = 0
@@ -203,14 +206,18 @@ def token_planted(seed: int = 6, N: int = 32768, H: int = 8, block: int = 64, n_
 def mixed_layer(seed: int = 3, N: int = 131072, H: int = 32, Hkv: int = 8, period: int = 4096,
                 n_vert: int = 64, last_q: int = 64, sink: int = 128, local: int = 2048,
                 nv: int = 1000, ns: int = 4096, block: int = 64, topk: int = 128,
-                n_ashape: int = 11, n_vs: int = 16) -> Workload:
+                n_ashape: int = 11, n_vs: int = 16, vs_rule: str = "last_q", nv_blocks: int = 16,
+                ns_blocks: int = 32) -> Workload:
     """Periodic slash structure plus planted vertical keys.
 
     Slash: dims 0-1 of every q and k at position t get a*(cos 2 pi t/P, sin 2 pi t/P)
     with a^2 = 3 sqrt(d), which adds 3 cos(2 pi (i-j)/P) to the logit of (i, j):
     offsets near multiples of P are favoured.  Vertical: per KV head, `n_vert`
     distinct key rows in [0, N - last_q) are set to 4 x the direction of the mean
-    of the group's last `last_q` queries (over all its Q heads)."""
+    of the group's last `last_q` queries (over all its Q heads).  vs_rule
+    "pooled" plans the Vertical-Slash heads with sets discovered from the
+    pooled block scores (nv_blocks key blocks, ns_blocks block offsets of
+    `block`) instead of last_q scoring; the data are the same."""
     g = _gen(seed)
     q, k, v = _qkv(g, 1, H, Hkv, N)
     t = torch.arange(N, dtype=torch.float64)
@@ -236,6 +243,8 @@ def mixed_layer(seed: int = 3, N: int = 131072, H: int = 32, Hkv: int = 8, perio
     for h in range(H):
         if h < n_ashape:
             plan.append(HeadPlan(VS, sink=sink, local=local, ashape=True))
+        elif h < n_ashape + n_vs and vs_rule == "pooled":
+            plan.append(HeadPlan(VS, pooled=True, block=block, nv_blocks=nv_blocks, ns_blocks=ns_blocks))
         elif h < n_ashape + n_vs:
             plan.append(HeadPlan(VS, last_q=last_q, nv=nv, ns=ns))
         else:

@@ -1,5 +1,6 @@
 """Shared helpers of the GPU parity tests: oracle index sets, the cutoff band
 rule for comparing selections, and oracle attention on given index sets."""
+import itertools
 import math
 
 import numpy as np
@@ -89,6 +90,10 @@ def oracle_head_sets(w, b, h):
     if p.kind == dsa.VS and getattr(p, "ashape", False):
         V, S = O.ashape_sets(Nk, p.sink, p.local)
         return ("vs", V, S, None, None)
+    if p.kind == dsa.VS and getattr(p, "pooled", False):
+        cols, diags, vbar, sbar, Vb, Sb = O.pooled_vs_sets(f64(w.q[b, h]), f64(w.k[b, kvh]), p.block, p.nv_blocks,
+                                                           p.ns_blocks)
+        return ("vs", cols, diags, vbar, sbar)
     if p.kind == dsa.VS:
         q = f64(w.q[b, h, Nq - p.last_q:])
         k = f64(w.k[b, kvh])
@@ -211,3 +216,28 @@ def check_hier_row(qf_i, kf, wf_i, p, route, cand, topk, kbar, g_route, g_cands,
     sel2, c2, tol2 = band_topk(dense, members, topk)
     assert_set_matches(g_tok, dense, sel2, c2, tol2, expect_count=min(topk, len(members)), what=f"{what} tokens")
     return True
+
+
+def check_pooled_sets(g_cols, g_diags, vbar, sbar, block, nvb, nsb, N, what=""):
+    """The GPU's Vertical-Slash set of a head with pooled discovery against the
+    oracle's masses vbar / sbar: the key blocks behind the columns match the
+    oracle's top-nv_blocks within the relative cutoff band and the columns are
+    exactly their keys; the diagonals are exactly the expansion of a top-ns_blocks
+    offset set that differs from the oracle's only inside the band."""
+    g_cols = np.asarray(g_cols, dtype=np.int64)
+    g_diags = np.asarray(g_diags, dtype=np.int64)
+    gb = np.unique(g_cols // block)
+    sel, c, tol = band_topk(vbar, np.arange(len(vbar)), nvb, rel_only=True)
+    assert_set_matches(gb, vbar, sel, c, tol, expect_count=min(nvb, len(vbar)), what=f"{what} key blocks")
+    assert np.array_equal(g_cols, O.expand_blocks(gb, [], block, N)[0]), f"{what}: columns are not whole blocks"
+    sel, c, tol = band_topk(sbar, np.arange(len(sbar)), nsb, rel_only=True)
+    if c is None:
+        cands = [sorted(sel)]
+    else:
+        band = [j for j in range(len(sbar)) if abs(sbar[j] - c) <= tol]
+        fixed = [j for j in sel if j not in band]
+        need = min(nsb, len(sbar)) - len(fixed)
+        assert len(band) <= 12, f"{what}: {len(band)} offsets inside the band"
+        cands = [sorted(fixed + list(x)) for x in itertools.combinations(band, need)]
+    ok = any(np.array_equal(g_diags, O.expand_blocks([], cs, block, N)[1]) for cs in cands)
+    assert ok, f"{what}: diagonals are not the expansion of the top block offsets"

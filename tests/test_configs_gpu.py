@@ -22,7 +22,7 @@ import dynamic_sparse_attention_mean_amd as dsa
 from dynamic_sparse_attention_mean_amd.pipeline import SparsePrefillLayer
 
 from parity import (MAX_ABS, MEAN_ABS, assert_set_matches, band_topk, check_block_selection, check_hier_row,
-                    f64, oracle_head_sets, row_set)
+                    check_pooled_sets, f64, oracle_head_sets, row_set)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -135,6 +135,12 @@ def check_sets(w, layer, heads, osets):
             assert int(layer.vs_index.diags_count[0, h]) == min(p.local, Nk)
             assert layer.vs_index.cols[0, h, :min(p.sink, Nk)].tolist() == list(range(min(p.sink, Nk)))
             assert layer.vs_index.diags[0, h, :min(p.local, Nk)].tolist() == list(range(min(p.local, Nk)))
+        elif p.kind == dsa.VS and p.pooled:
+            _, _, _, vbar, sbar = osets[h]
+            vsi = layer.vs_index
+            check_pooled_sets(vsi.cols[0, h, :int(vsi.cols_count[0, h])].cpu().numpy(),
+                              vsi.diags[0, h, :int(vsi.diags_count[0, h])].cpu().numpy(), vbar, sbar, p.block,
+                              p.nv_blocks, p.ns_blocks, Nk, what=f"head {h}")
         elif p.kind == dsa.VS:
             _, _, _, v, s = osets[h]
             for name, sc, k, g, cnt in (("cols", v, p.nv, layer.vs_index.cols, layer.vs_index.cols_count),
@@ -195,6 +201,17 @@ def test_config3_mixed_128k():
     os_ = osets_of(w, range(32))
     check_sets(w, layer, range(32), os_)
     check_rows(w, layer, o, lse, range(32), os_, rows_per_head=24, o32=o32)
+
+
+def test_config3_pooled_discovery_128k():
+    """The 128K mixed layer with its Vertical-Slash heads (11-26) discovered
+    from pooled block scores (block 64, 16 key blocks, 32 block offsets): every
+    head's sets against the oracle's, sampled rows of every head."""
+    w = synth.config(3, vs_rule="pooled")
+    layer, o, lse, o32 = run_layer(w)
+    os_ = osets_of(w, range(32))
+    check_sets(w, layer, range(32), os_)
+    check_rows(w, layer, o, lse, range(32), os_, rows_per_head=12, o32=o32)
 
 
 def test_config4_threshold_4k_every_row():

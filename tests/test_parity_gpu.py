@@ -11,8 +11,8 @@ import synth
 import dynamic_sparse_attention_mean_amd as dsa
 from dynamic_sparse_attention_mean_amd.pipeline import SparsePrefillLayer
 
-from parity import (assert_attention_close, assert_set_matches, band_topk, check_block_selection, f64,
-                    oracle_attention_rows, oracle_head_sets, upload_sets)
+from parity import (assert_attention_close, assert_set_matches, band_topk, check_block_selection, check_pooled_sets,
+                    f64, oracle_attention_rows, oracle_head_sets, upload_sets)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -38,7 +38,8 @@ def all_rows_check(w, sets, o, lse, what):
 @pytest.mark.parametrize("N,block,mode,force", [(1000, 64, "topk", True), (2048, 64, "topk", False),
                                                 (1100, 128, "thresh", False), (777, 64, "thresh", True),
                                                 (1000, 32, "topk", True), (700, 16, "thresh", False),
-                                                (513, 16, "topk", False)])
+                                                (513, 16, "topk", False), (8192, 64, "topk", True),
+                                                (4100, 32, "thresh", True)])
 def test_block_index_parity(N, block, mode, force):
     w = synth.block_planted(seed=20 + N, H=3, Hkv=1, N=N, block=block, n_plant=3, mode=mode, topk=4, force=force)
     q, k, _ = dev(w)
@@ -164,6 +165,39 @@ def test_vs_index_parity(N, last_q, nv, ns):
         sel, c, tol = band_topk(sc, np.arange(N), kk, rel_only=True)
         n = int(cnt[0, 0].item())
         assert_set_matches(g[0, 0, :n].cpu().numpy(), sc, sel, c, tol, expect_count=min(kk, N), what=name)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,block,nvb,nsb,heads", [(1, 2, 1, 1000, 64, 3, 4, [0, 1]),
+                                                        (2, 4, 2, 2048 + 37, 32, 8, 10, [3, 0, 2]),
+                                                        (1, 2, 2, 4100, 16, 20, 30, [1]),
+                                                        (1, 1, 1, 1500, 128, 2, 5, [0]),
+                                                        (1, 2, 1, 700, 64, 11, 11, [1, 0])])
+def test_vs_pooled_parity(B, H, Hkv, N, block, nvb, nsb, heads):
+    """Vertical-Slash sets from pooled block scores: the vertical and slash
+    masses (listed order) against the oracle's, the key blocks and block
+    offsets within the band, the token columns and diagonals exactly their
+    expansion; ragged N, batch 2, heads out of order, budgets above the
+    number of blocks (every block kept)."""
+    w = synth.vs_multi(seed=80 + N + block, B=B, H=H, Hkv=Hkv, Nk=N, n_plant=6)
+    q, k, _ = dev(w)
+    nb = -(-N // block)
+    out = dsa.VSIndex.empty(B, H, min(N, nvb * block), min(N, nsb * (2 * block - 1)), DEV)
+    vsc = torch.zeros(B, len(heads), nb, device=DEV)
+    ssc = torch.zeros(B, len(heads), nb, device=DEV)
+    dsa.build_index_vs_pooled(q, k, heads, block, nvb, nsb, out, v_scores=vsc, s_scores=ssc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for t, h in enumerate(heads):
+            cols, diags, vbar, sbar, Vb, Sb = O.pooled_vs_sets(f64(w.q[b, h]), f64(w.k[b, h // (H // Hkv)]), block,
+                                                               nvb, nsb)
+            for name, got, ref in (("vbar", vsc[b, t], vbar), ("sbar", ssc[b, t], sbar)):
+                g = got.cpu().double().numpy()
+                tol = 1e-5 * np.abs(ref) + 1e-7 * ref.sum() / len(ref)
+                assert np.all(np.abs(g - ref) <= tol), f"b{b} h{h} {name}: {np.abs(g - ref).max():.3g}"
+            assert abs(vsc[b, t].sum().item() - nb) < 1e-3 * nb and abs(ssc[b, t].sum().item() - nb) < 1e-3 * nb
+            check_pooled_sets(out.cols[b, h, :int(out.cols_count[b, h])].cpu().numpy(),
+                              out.diags[b, h, :int(out.diags_count[b, h])].cpu().numpy(), vbar, sbar, block, nvb,
+                              nsb, N, what=f"b{b} h{h}")
 
 
 def test_ashape_sets():
