@@ -28,6 +28,7 @@ OP_VS, OP_BLOCK, OP_TOKENS, OP_ATTN, OP_TOKENS_HIER, OP_VS_POOLED = 1, 2, 3, 4, 
 EXPORTS = (
     "dsa_status_string", "dsa_last_error", "dsa_workspace_size", "build_index_ashape",
     "build_index_vs", "build_index_vs_pooled", "build_index_block", "build_index_tokens", "build_index_tokens_hier", "sparse_prefill_attn",
+    "sparse_prefill_attn_noalloc",
 )
 
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_prefill_attn.argtypes = [ctypes.POINTER(Shape), P, P, P, P, ctypes.POINTER(_VsIndexC),
                                           ctypes.POINTER(_BlockIndexC), ctypes.POINTER(_TokenIndexC), I32, P, P, P,
                                           SZ, P]
+        L.sparse_prefill_attn_noalloc.restype = I32
+        L.sparse_prefill_attn_noalloc.argtypes = [ctypes.POINTER(Shape), P, P, P, P, ctypes.POINTER(_VsIndexC),
+                                                  ctypes.POINTER(_BlockIndexC), ctypes.POINTER(_TokenIndexC), I32, P,
+                                                  P, P]
         _lib = L
     return _lib
 
@@ -307,3 +312,27 @@ def sparse_prefill_attn(q, k, v, head_kind, vs: Optional[VSIndex] = None, blk: O
            "sparse_prefill_attn")
     return o, lse
 
+
+def sparse_prefill_attn_noalloc(q, k, v, head_kind, o, lse=None, vs: Optional[VSIndex] = None,
+                                blk: Optional[BlockIndex] = None, tok: Optional[TokenIndex] = None, out_dtype=OUT_F32):
+    """sparse_prefill_attn with the library's static scratch instead of a
+    workspace: nothing is allocated, the caller passes the outputs (o, and lse
+    or None).  Calls that overlap on one device race."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    _need(v, "v", torch.bfloat16, q.device)
+    _need(o, "o", torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, q.device)
+    shape = make_shape(q, k)
+    kinds = (ctypes.c_int32 * q.shape[1])(*[int(x) for x in head_kind])
+    vsc = vs.c() if vs is not None else None
+    bc = blk.c() if blk is not None else None
+    tc = tok.c() if tok is not None else None
+    _check(lib().sparse_prefill_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), kinds,
+                                             ctypes.byref(vsc) if vsc is not None else None,
+                                             ctypes.byref(bc) if bc is not None else None,
+                                             ctypes.byref(tc) if tc is not None else None,
+                                             out_dtype, _ptr(o), _ptr(lse), _stream(q.device)),
+           "sparse_prefill_attn_noalloc")
+    return o, lse

@@ -430,11 +430,14 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
   return hip_status(launch_indexer(a, ws_base(ws), (hipStream_t)stream), "build_index_tokens_hier");
 }
 
-dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
-                               const int32_t* head_kind, const dsa_vs_index* vs, const dsa_block_index* blk,
-                               const dsa_token_index* tok, int32_t out_dtype, void* o, float* lse, void* ws,
-                               size_t ws_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Argument checks and kernel arguments shared by both attention entry points.
+dsa_status prepare_attn(const dsa_shape* shape, const void* q, const void* k, const void* v, const int32_t* head_kind,
+                        const dsa_vs_index* vs, const dsa_block_index* blk, const dsa_token_index* tok,
+                        int32_t out_dtype, void* o, float* lse, AttnArgs& a) {
   dsa_status st = check_shape(shape);
   if (st) return st;
   if (!q || !k || !v || !o) return fail(DSA_ERR_INVALID_ARG, "q, k, v or o is null");
@@ -442,7 +445,6 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
     return fail(DSA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (!head_kind) return fail(DSA_ERR_INVALID_ARG, "head_kind is null");
   if (out_dtype != DSA_OUT_BF16 && out_dtype != DSA_OUT_F32) return fail(DSA_ERR_INVALID_ARG, "out_dtype");
-  AttnArgs a;
   std::memset(&a, 0, sizeof a);
   bool use[4] = {};
   for (int h = 0; h < shape->heads; ++h) {
@@ -463,9 +465,6 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
     if (!tok || !tok->idx || !tok->count || tok->cap < 1) return fail(DSA_ERR_INVALID_ARG, "token heads need a token index set");
     if (tok->cap > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "more than %d tokens per query", kMaxTokensPerQuery);
   }
-  const size_t need = ws_attn(shape);
-  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = o; a.lse = lse; a.out_f32 = out_dtype == DSA_OUT_F32;
   a.B = shape->batch; a.H = shape->heads; a.Hkv = shape->kv_heads;
@@ -481,7 +480,43 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
   if (use[DSA_PATTERN_TOKEN]) {
     a.tidx = tok->idx; a.tcount = tok->count; a.tcap = tok->cap;
   }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                               const int32_t* head_kind, const dsa_vs_index* vs, const dsa_block_index* blk,
+                               const dsa_token_index* tok, int32_t out_dtype, void* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_err.clear();
+  AttnArgs a;
+  dsa_status st = prepare_attn(shape, q, k, v, head_kind, vs, blk, tok, out_dtype, o, lse, a);
+  if (st) return st;
+  const size_t need = ws_attn(shape);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(launch_attention(a, ws_base(ws), (hipStream_t)stream), "sparse_prefill_attn");
+}
+
+dsa_status sparse_prefill_attn_noalloc(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                                       const int32_t* head_kind, const dsa_vs_index* vs, const dsa_block_index* blk,
+                                       const dsa_token_index* tok, int32_t out_dtype, void* o, float* lse,
+                                       void* stream) {
+  g_err.clear();
+  AttnArgs a;
+  dsa_status st = prepare_attn(shape, q, k, v, head_kind, vs, blk, tok, out_dtype, o, lse, a);
+  if (st) return st;
+  const size_t need = attn_workspace_bytes(shape->batch, shape->heads, shape->kv_len);
+  if (need > kStaticScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "sparse_prefill_attn_noalloc: this shape needs %zu bytes of scratch, the static buffer holds %zu "
+                "(use sparse_prefill_attn with a workspace)",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = hip_status(static_scratch(&ws), "sparse_prefill_attn_noalloc: scratch address"))) return st;
+  return hip_status(launch_attention(a, ws, (hipStream_t)stream), "sparse_prefill_attn_noalloc");
 }
 
 }  // extern "C"

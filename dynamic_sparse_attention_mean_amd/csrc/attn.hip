@@ -45,6 +45,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1003,6 +1004,33 @@ VsLayout vs_layout(int B, int H, int Nk) {
 }
 
 }  // namespace
+
+// Scratch of the attention entry point that allocates nothing (for callers
+// that cannot call hipMalloc): one copy of this array lives on every device the
+// library runs on, until the process ends.  Host code never uses the array's
+// name as an address: the per-device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t attn_workspace_bytes(int B, int H, int Nk) {
   VsLayout L = vs_layout(B, H, Nk);

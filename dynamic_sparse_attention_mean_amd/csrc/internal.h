@@ -114,6 +114,11 @@ struct AttnArgs {
 };
 size_t attn_workspace_bytes(int B, int H, int Nk);
 hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st);
+// The attention scratch of the entry point that allocates nothing: a static
+// device array of kStaticScratchBytes; *ptr receives its address on the
+// current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
 
 // --------------------------------------------------------------- indexer
 struct IndexerArgs {

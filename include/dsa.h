@@ -260,6 +260,22 @@ dsa_status sparse_prefill_attn(const dsa_shape* shape, const void* q, const void
                                const dsa_token_index* tok, int32_t out_dtype,
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* sparse_prefill_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results, with no workspace
+ * argument.  Its scratch is a static device array of 32 MiB that the library
+ * holds on every device it runs on until the process ends; shapes whose
+ * scratch (about B * H * Nk / 2 bytes) exceeds it return DSA_ERR_UNSUPPORTED
+ * and must use sparse_prefill_attn.  The call itself allocates nothing.  All
+ * calls on one device share that array and the call clears what it needs
+ * first: calls that overlap in time on one device (different streams, or
+ * different threads) race and give undefined results. */
+dsa_status sparse_prefill_attn_noalloc(const dsa_shape* shape, const void* q, const void* k,
+                                       const void* v, const int32_t* head_kind,
+                                       const dsa_vs_index* vs, const dsa_block_index* blk,
+                                       const dsa_token_index* tok, int32_t out_dtype,
+                                       void* o, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
