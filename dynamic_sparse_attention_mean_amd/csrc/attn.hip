@@ -253,13 +253,16 @@ struct Item {
   int nent, ngather;
 };
 
-// Cursor over a pair's entries.  The global-memory lookups of entry n + 1 are
-// issued while entry n is being processed (one step of prefetch).
+// Cursor over a pair's entries.  The list lookups an entry will need are
+// issued by cursor_fetch() at the end of the step before (one step of
+// prefetch), after that step's LDS reads: scalar loads share the LDS reads'
+// wait counter.
 struct Cursor {
   int n;                   // index of the next entry
   int raw;                 // prefetched value for entry n (shared block list)
   int i0, i1, x0, x1;      // two-list merge state (block 64): heads of both lists
   int x0n, x1n;            // prefetched successors of the heads
+  bool fetch_raw, fetch0, fetch1;   // lookups cursor_fetch() still has to issue
 };
 
 __device__ __forceinline__ int list_at(const int32_t* L, int n, int i) { return i < n ? ldc(L, i) : 0x7fffffff; }
@@ -267,6 +270,7 @@ __device__ __forceinline__ int list_at(const int32_t* L, int n, int i) { return 
 __device__ __forceinline__ void cursor_init(const Item& it, Cursor& c) {
   c.n = 0;
   c.raw = 0;
+  c.fetch_raw = c.fetch0 = c.fetch1 = false;
   c.i0 = c.i1 = 0;
   c.x0 = c.x1 = c.x0n = c.x1n = 0x7fffffff;
   if (it.kind == 2 && it.per == 2) c.raw = it.n0 > 0 ? ldc(it.l0, 0) : 0;
@@ -294,13 +298,13 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
     e.cnt = min(TK, it.ngather - n * TK);
   } else if (it.kind == 2 && it.per == 2) {
     e.kt = c.raw * 2 + (n & 1);
-    if (n & 1) c.raw = ((n >> 1) + 1 < it.n0) ? ldc(it.l0, (n >> 1) + 1) : 0;
+    c.fetch_raw = (n & 1) != 0;            // entry n + 1 starts the next list element
   } else if (it.kind == 2) {
     const int x = min(c.x0, c.x1);
     e.kt = x;
     e.flags = (c.x0 == x ? 1 : 0) | (c.x1 == x ? 2 : 0);
-    if (c.x0 == x) { ++c.i0; c.x0 = c.x0n; c.x0n = list_at(it.l0, it.n0, c.i0 + 1); }
-    if (c.x1 == x) { ++c.i1; c.x1 = c.x1n; c.x1n = list_at(it.l1, it.n1, c.i1 + 1); }
+    if (c.x0 == x) { ++c.i0; c.x0 = c.x0n; c.fetch0 = true; }
+    if (c.x1 == x) { ++c.i1; c.x1 = c.x1n; c.fetch1 = true; }
   } else if (it.kind == 3) {
     e.kt = n < it.n0 ? n : it.n1 + (n - it.n0);
   } else {
@@ -309,6 +313,14 @@ __device__ __forceinline__ Entry cursor_next(const Item& it, Cursor& c) {
   // out-of-range block ids or tiles beyond the pair's last row contribute nothing
   if (e.kind == 0 && (e.kt < 0 || e.kt * TK > it.last_pos)) e.flags = 0;
   return e;
+}
+
+// The list lookups the last cursor_next() left for later (see Cursor).
+__device__ __forceinline__ void cursor_fetch(const Item& it, Cursor& c) {
+  if (c.fetch_raw) c.raw = ((c.n >> 1) < it.n0) ? ldc(it.l0, c.n >> 1) : 0;
+  if (c.fetch0) c.x0n = list_at(it.l0, it.n0, c.i0 + 1);
+  if (c.fetch1) c.x1n = list_at(it.l1, it.n1, c.i1 + 1);
+  c.fetch_raw = c.fetch0 = c.fetch1 = false;
 }
 
 // DMA of one 64-key tile of K or V into LDS.  Wave w fills the 1 KB blocks
@@ -703,9 +715,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
                 if (mod5(v - (4 - ec)) == 0) issue_block(v);
             }
-            // the next step's words and the list entry after it
-            const StepWords wn = load_words(en);
-            const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
             if (active) {
               // lane row r sees offsets 32 ec + r - c for keys c = 0..31
               const uint64_t dwin = ((uint64_t)wc.d1 << 32) | wc.d0;
@@ -719,6 +728,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const int sl = mod5(u);
               sub32(sl * SLOT, sl * SLOT + 8192, M);
             }
+            // The next step's words and the list entry after it, issued once
+            // this step's LDS reads are done: scalar loads and LDS reads share
+            // one counter, so issued earlier, the step's first LDS wait would
+            // also wait for them.  Here their latency overlaps the next step's
+            // DMA wait and barrier.
+            const StepWords wn = load_words(en);
+            const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
             if (--k < 0) break;
             ep = ec;
             ec = en;
@@ -855,6 +871,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           cur = cursor_next(it, cc);
           issue_tile<false>(kbp, a.Nk, cur, s_cols, ring, w, l, off_k);
           issue_tile<true>(vbp, a.Nk, cur, s_cols, ring + TK * 256, w, l, off_v);
+          cursor_fetch(it, cc);
         }
         take_q();
         // One tile step on ring stage `stage` (a compile-time constant, so every
@@ -922,6 +939,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             Mk[kb] = M;
           }
           sub64(stage * 2 * TK * 256, (stage * 2 + 1) * TK * 256, Mk[0], Mk[1]);
+          cursor_fetch(it, cc);                  // after the step's LDS reads (see Cursor)
           cur = nxt;
           have = have_n;
         };
