@@ -76,6 +76,14 @@ struct VsScoreArgs {
   float* part_diag;       // [B, n_heads, nchunks, chunk_keys + 64] per-chunk diagonal sums
   int nchunks, chunk_tiles;
 };
+// Listed heads grouped by KV head for the scoring passes: group s holds the
+// listed indices order[first[s] .. first[s] + cnt[s]) (at most 4, one KV head).
+struct VsGroupTable {
+  int32_t n;
+  int16_t first[256];
+  int16_t order[256];
+  int8_t cnt[256];
+};
 size_t vs_workspace_floats(int n_rows, int Nk);   // n_rows = B * n_heads
 hipError_t launch_vs_scores(const VsScoreArgs& a, hipStream_t st);
 

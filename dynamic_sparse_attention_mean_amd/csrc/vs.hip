@@ -8,7 +8,8 @@
 //   p[r, j] = softmax_j(q_r . k_j / sqrt(d)) over j <= p_r = Nk - L + r
 //   v[j] = sum_r p[r, j]        s[o] = sum_r p[r, p_r - o]
 //
-// Two passes over K per head on v_mfma_f32_32x32x16_bf16: pass 1 finds each
+// Two passes over K on v_mfma_f32_32x32x16_bf16, one workgroup per group of
+// listed heads that share a KV head (and per chunk of keys): pass 1 finds each
 // row's max and sum of exponentials; pass 2 forms the normalised p and reduces
 // it along columns and diagonals.  Every reduction runs in a fixed order, so v
 // and s are bitwise reproducible.
@@ -38,177 +39,227 @@ __device__ __forceinline__ void load_qfrag(const VsScoreArgs& a, int b, int h, i
   }
 }
 
-// K fragments of keys kt*64 + 32 kb + (0..31) (zero beyond Nk).
-struct KFrag {
-  u32x4 x[8];
-};
-__device__ __forceinline__ void load_kfrag(const uint16_t* kp, int Nk, int kt, int kb, KFrag& k) {
-  const int l = threadIdx.x & 63, hh = l >> 5;
-  const int key = kt * 64 + 32 * kb + (l & 31);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < Nk) x = *(const u32x4*)(kp + (size_t)key * 128 + 16 * ks + 8 * hh);
-    k.x[ks] = x;
-  }
+constexpr float kScale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+// ---------------------------------------------------------------------------
+// The two passes per KV group: a workgroup takes up to GH listed heads that
+// read the same KV head (two waves per head: query rows 0-31 and 32-63), so
+// each 32-key block of K is brought into LDS once (DMA) for all of them.
+// Per block a wave forms S^T for its 32 rows on v_mfma_f32_32x32x16_bf16 with
+// the K fragments read from LDS.  Pass 2 stages each head's weights in LDS and
+// reduces them along columns (four lanes per column, rows in a fixed order)
+// and diagonals (one lane per diagonal, rows ascending).
+constexpr int GH = 4;                // heads per workgroup
+constexpr int GT = 2 * GH * 64;      // threads: wave w serves head slot w / 2, rows 32 (w % 2) ..
+constexpr int KB = 32;               // keys per block
+constexpr int CKB = CK / KB;         // blocks per chunk
+
+typedef __attribute__((address_space(3))) void lds_void_vs_t;
+__device__ __forceinline__ void vs_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ int vs_swz(int r, int c) { return c ^ (r & 15); }
+
+// DMA of K block kb (32 keys, 8 KB) into an LDS stage: lane l of wave w takes
+// row 4 w + l / 16 and writes LDS chunk l % 16 of that row, which holds the
+// row's 16-byte chunk (l % 16) ^ (row % 16); keys past the end are clamped.
+__device__ __forceinline__ void vs_issue_block(const uint16_t* kp, int Nk, int kb, char* stage) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r = 4 * w + (l >> 4);
+  const int key = min(kb * KB + r, Nk - 1);
+  const int c = vs_swz(r, l & 15);
+  __builtin_amdgcn_global_load_lds(kp + (size_t)key * 128 + c * 8, (lds_void_vs_t*)(stage + w * 1024), 16, 0, 0);
 }
 
-// S^T block: those keys against this wave's 32 query rows.
-__device__ __forceinline__ f32x16 score_block(const KFrag& k, const Frag& f) {
+// S^T of one 32-key block against this wave's 32 query rows, K from LDS.
+__device__ __forceinline__ f32x16 vs_block_scores(const char* stage, const Frag& f) {
+  const int l = threadIdx.x & 63, qn = l & 31, hh = l >> 5;
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  u32x4 kf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(stage + qn * 256 + vs_swz(qn, 2 * ks + hh) * 16);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k.x[ks]), f.q[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), f.q[ks], acc, 0, 0, 0);
   return acc;
 }
 
-constexpr float kScale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+struct VsGroupInfo {
+  int ng, hi, h, kvh;                // heads in the group, this wave's listed index and head, KV head
+  bool on;                           // this wave's head slot is used
+};
+__device__ __forceinline__ VsGroupInfo vs_group_info(const VsScoreArgs& a, const VsGroupTable& t) {
+  VsGroupInfo gi;
+  const int sg = blockIdx.x;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  gi.ng = t.cnt[sg];
+  gi.on = g < gi.ng;
+  gi.hi = t.order[t.first[sg] + (gi.on ? g : 0)];
+  gi.h = a.heads.h[gi.hi];
+  gi.kvh = a.heads.h[t.order[t.first[sg]]] / (a.H / a.Hkv);
+  return gi;
+}
 
-__global__ __launch_bounds__(256) void vs_pass1_kernel(VsScoreArgs a) {
-  __shared__ float s_m[2][64], s_l[2][64];
-  const int hi = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int h = a.heads.h[hi];
-  const int kvh = h / (a.H / a.Hkv);
+// Wait until at most n of this wave's DMAs are outstanding (n = 0, 1, 2).
+__device__ __forceinline__ void vs_wait_vm_upto(int n) {
+  if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+constexpr int P1ST = 4;              // pass 1 ring stages: blocks prefetched three ahead
+
+__global__ __launch_bounds__(GT) void vs_group_pass1_kernel(VsScoreArgs a, VsGroupTable t) {
+  __shared__ __align__(1024) char s_k[P1ST][KB * 256];
+  const int c = blockIdx.y, b = blockIdx.z;
+  const VsGroupInfo gi = vs_group_info(a, t);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hh = l >> 5, qn = l & 31;
-  const int kb = w & 1, qb = w >> 1;
-  const int r = 32 * qb + qn;
+  const int r = 32 * (w & 1) + qn;
   const int pr = a.Nk - a.last_q + r;
   Frag f;
-  load_qfrag(a, b, h, r, f);
-  const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * a.Nk) * 128;
+  load_qfrag(a, b, gi.h, gi.on ? r : 64, f);           // rows >= last_q load zeros
+  const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + gi.kvh) * a.Nk) * 128;
+  const int nblk = (a.Nk + KB - 1) / KB;
+  const int kb0 = c * CKB, kb1 = min(nblk, kb0 + CKB);
   float m = -INFINITY, s = 0.f;
-  const int kt_end = min((c + 1) * CH, (a.Nk + 63) / 64);
-  KFrag kn;
-  if (c * CH < kt_end) load_kfrag(kp, a.Nk, c * CH, kb, kn);
-  for (int kt = c * CH; kt < kt_end; ++kt) {
-    const KFrag kc = kn;
-    if (kt + 1 < kt_end) load_kfrag(kp, a.Nk, kt + 1, kb, kn);   // one tile ahead
-    const f32x16 acc = score_block(kc, f);
-    float z[16];
-    float mt = -INFINITY;
+  // the loop stores nothing, so DMAs are this wave's only vector memory
+  // operations and complete in issue order: a partial count is safe
+  for (int i = 0; i < P1ST - 1 && kb0 + i < kb1; ++i) vs_issue_block(kp, a.Nk, kb0 + i, s_k[i]);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int st = (kb - kb0) % P1ST;
+    vs_wait_vm_upto(min(P1ST - 2, kb1 - 1 - kb));     // block kb landed (later ones may be in flight)
+    __syncthreads();                                  // ... for every wave; all are done with kb - 1
+    if (kb + P1ST - 1 < kb1) vs_issue_block(kp, a.Nk, kb + P1ST - 1, s_k[(st + P1ST - 1) % P1ST]);
+    if (gi.on) {
+      const f32x16 acc = vs_block_scores(s_k[st], f);
+      float z[16];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kt * 64 + 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const bool ok = key < a.Nk && key <= pr && r < a.last_q;
-      z[v] = ok ? acc[v] * kScale2 : -INFINITY;
-      mt = fmaxf(mt, z[v]);
-    }
-    if (mt > -INFINITY) {
-      const float mn = fmaxf(m, mt);
-      float add = 0.f;
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * KB + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const bool ok = key < a.Nk && key <= pr && r < a.last_q;
+        z[v] = ok ? acc[v] * kScale2 : -INFINITY;
+        mt = fmaxf(mt, z[v]);
+      }
+      if (mt > -INFINITY) {
+        const float mn = fmaxf(m, mt);
+        float add = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(z[v] - mn);
-      s = s * __builtin_amdgcn_exp2f(m - mn) + add;
-      m = mn;
+        for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(z[v] - mn);
+        s = s * __builtin_amdgcn_exp2f(m - mn) + add;
+        m = mn;
+      }
     }
   }
-  // combine the two lanes of each query (hh = 0, 1), then the two key halves
+  // the row's two lanes (hh = 0, 1), combined in the same order on both
   const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64);
   const float mm = fmaxf(m, m2);
   const float ss = (mm == -INFINITY) ? 0.f
                    : (hh == 0 ? s * __builtin_amdgcn_exp2f(m - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm)
                               : s2 * __builtin_amdgcn_exp2f(m2 - mm) + s * __builtin_amdgcn_exp2f(m - mm));
-  if (hh == 0) { s_m[kb][r] = mm; s_l[kb][r] = ss; }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int rr = threadIdx.x;
-    const float ma = s_m[0][rr], mb = s_m[1][rr];
-    const float mm2 = fmaxf(ma, mb);
-    const float ll = (mm2 == -INFINITY) ? 0.f
-                     : s_l[0][rr] * __builtin_amdgcn_exp2f(ma - mm2) + s_l[1][rr] * __builtin_amdgcn_exp2f(mb - mm2);
-    float* pm = a.part_ml + (((size_t)(b * a.heads.n + hi) * a.nchunks + c) * 2) * 64;
-    pm[rr] = mm2;
-    pm[64 + rr] = ll;
+  if (gi.on && hh == 0) {
+    float* pm = a.part_ml + (((size_t)(b * a.heads.n + gi.hi) * a.nchunks + c) * 2) * 64;
+    pm[r] = mm;
+    pm[64 + r] = ss;
   }
 }
 
-__global__ __launch_bounds__(256) void vs_pass2_kernel(VsScoreArgs a) {
-  __shared__ float s_p[64 * 65];
-  __shared__ float s_diag[DSPAN];
-  __shared__ float s_mr[64], s_il[64];
-  const int hi = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int h = a.heads.h[hi];
-  const int kvh = h / (a.H / a.Hkv);
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, hh = l >> 5, qn = l & 31;
-  const int kb = w & 1, qb = w >> 1;
-  const int r = 32 * qb + qn;
+__global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGroupTable t) {
+  __shared__ __align__(1024) char s_k[2][KB * 256];
+  __shared__ float s_p[GH][64 * (KB + 1)];
+  __shared__ float s_diag[GH][DSPAN];
+  __shared__ float s_mr[GH][64], s_il[GH][64];
+  const int c = blockIdx.y, b = blockIdx.z;
+  const VsGroupInfo gi = vs_group_info(a, t);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hh = l >> 5, qn = l & 31;
+  const int g = w >> 1;
+  const int r = 32 * (w & 1) + qn;
   const int pr = a.Nk - a.last_q + r;
-  const size_t row = (size_t)(b * a.heads.n + hi);
+  const size_t row = (size_t)(b * a.heads.n + gi.hi);
 
-  if (tid < 64) {
-    // final row max and sum, combined over all chunks in ascending order
+  // final row max and sum of each head, over all chunks in ascending order
+  if ((w & 1) == 0 && gi.on) {
     const float* pm = a.part_ml + (row * a.nchunks) * 128;
     float m = -INFINITY, s = 0.f;
     for (int cc = 0; cc < a.nchunks; ++cc) {
-      const float mc = pm[cc * 128 + tid], sc = pm[cc * 128 + 64 + tid];
+      const float mc = pm[cc * 128 + l], sc = pm[cc * 128 + 64 + l];
       const float mn = fmaxf(m, mc);
       if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m - mn) + sc * __builtin_amdgcn_exp2f(mc - mn);
       m = mn;
     }
-    s_mr[tid] = m;
-    s_il[tid] = s > 0.f ? 1.0f / s : 0.f;
+    s_mr[g][l] = m;
+    s_il[g][l] = s > 0.f ? 1.0f / s : 0.f;
   }
-  for (int i = tid; i < DSPAN; i += 256) s_diag[i] = 0.f;
-  __syncthreads();
-
+  for (int i = tid; i < GH * DSPAN; i += GT) (&s_diag[0][0])[i] = 0.f;
   Frag f;
-  load_qfrag(a, b, h, r, f);
-  const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * a.Nk) * 128;
-  const float mr = s_mr[r & 63], il = s_il[r & 63];
-  const int kt0 = c * CH;
-  const int kt_end = min((c + 1) * CH, (a.Nk + 63) / 64);
-  // offset of local diagonal slot 0 of this chunk
-  const int o_min = a.Nk - a.last_q - (kt0 + CH - 1) * 64 - 63;
+  load_qfrag(a, b, gi.h, gi.on ? r : 64, f);
+  const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + gi.kvh) * a.Nk) * 128;
+  const int nblk = (a.Nk + KB - 1) / KB;
+  const int kb0 = c * CKB, kb1 = min(nblk, kb0 + CKB);
+  const int o_min = a.Nk - a.last_q - (c + 1) * CK + 1;   // offset of diagonal slot 0 of this chunk
   float* vo = a.v_out + row * a.Nk;
-  KFrag kn;
-  if (kt0 < kt_end) load_kfrag(kp, a.Nk, kt0, kb, kn);
-  for (int kt = kt0; kt < kt_end; ++kt) {
-    const KFrag kc = kn;
-    if (kt + 1 < kt_end) load_kfrag(kp, a.Nk, kt + 1, kb, kn);   // one tile ahead
-    const f32x16 acc = score_block(kc, f);
+  float* sp = s_p[g];
+  const int tl = tid & 127;                               // this thread's place among its head's 128
+  vs_issue_block(kp, a.Nk, kb0, s_k[0]);
+  __syncthreads();                                        // row statistics visible
+  const float mr = s_mr[g][r & 63], il = s_il[g][r & 63];
+  // A block's column sums are stored at the start of the next block, right
+  // after its wait: stores and the DMA share one counter, so a store issued at
+  // the end of a block would hold up the next block's wait for the DMA.
+  float cs_pend = 0.f;
+  int col_pend = -1;
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int st = (kb - kb0) & 1;
+    vs_wait_vm();
+    __syncthreads();                                      // block kb landed; the last block's sums are done
+    if (col_pend >= 0) vo[col_pend] = cs_pend;
+    col_pend = -1;
+    if (kb + 1 < kb1) vs_issue_block(kp, a.Nk, kb + 1, s_k[st ^ 1]);
+    if (gi.on) {
+      const f32x16 acc = vs_block_scores(s_k[st], f);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int cc = 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const int key = kt * 64 + cc;
-      const bool ok = key < a.Nk && key <= pr && r < a.last_q;
-      s_p[r * 65 + cc] = ok ? __builtin_amdgcn_exp2f(acc[v] * kScale2 - mr) * il : 0.f;
-    }
-    __syncthreads();
-    {
-      // column sums: four lanes per column, 16 rows each, then (p0 + p1) + (p2 + p3)
-      const int col = tid >> 2, part = tid & 3;
-      float cs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cs += s_p[(16 * part + i) * 65 + col];
-      cs += __shfl_xor(cs, 1, 64);
-      cs += __shfl_xor(cs, 2, 64);
-      if (part == 0 && kt * 64 + col < a.Nk) vo[kt * 64 + col] = cs;
-    }
-    // diagonal sums: two lanes per diagonal dl = r - c (lower and upper rows of
-    // its range), then their sum; lanes 254 and 255 idle
-    {
-      const int dg = tid >> 1, part = tid & 1;
-      const int dl = min(dg, 126) - 63;
-      const int rlo = max(0, dl), rhi = min(63, 63 + dl);
-      const int rmid = (rlo + rhi + 1) >> 1;
-      float ds = 0.f;
-      if (dg < 127) {
-        const int r0 = part ? rmid : rlo, r1 = part ? rhi + 1 : rmid;
-        for (int rr = r0; rr < r1; ++rr) ds += s_p[rr * 65 + (rr - dl)];
-      }
-      ds += __shfl_xor(ds, 1, 64);
-      if (dg < 127 && part == 0) {
-        const int o = a.Nk - a.last_q - kt * 64 + dl;
-        s_diag[o - o_min] += ds;
+      for (int v = 0; v < 16; ++v) {
+        const int cc = 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int key = kb * KB + cc;
+        const bool ok = key < a.Nk && key <= pr && r < a.last_q;
+        sp[r * (KB + 1) + cc] = ok ? __builtin_amdgcn_exp2f(acc[v] * kScale2 - mr) * il : 0.f;
       }
     }
     __syncthreads();
+    if (gi.on) {
+      {
+        // column sums: four lanes per column, 16 rows each, then (p0 + p1) + (p2 + p3)
+        const int col = tl >> 2, part = tl & 3;
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cs += sp[(16 * part + i) * (KB + 1) + col];
+        cs += __shfl_xor(cs, 1, 64);
+        cs += __shfl_xor(cs, 2, 64);
+        if (part == 0 && kb * KB + col < a.Nk) { cs_pend = cs; col_pend = kb * KB + col; }
+      }
+      if (tl < 95) {
+        // diagonal dl = r - cc in [-31, 63]: the terms of keys cc = 0 .. 31 (rows
+        // dl + cc, ascending); a fixed count lets eight reads be in flight at a
+        // time.  Rows outside [0, 63] read row 0 (in bounds) and add nothing.
+        const int dl = tl - 31;
+        float ds = 0.f;
+#pragma unroll 8
+        for (int cc = 0; cc < KB; ++cc) {
+          const int rr = dl + cc;
+          const bool in = rr >= 0 && rr < 64;
+          const float x = sp[(in ? rr : 0) * (KB + 1) + cc];
+          ds += in ? x : 0.f;
+        }
+        s_diag[g][a.Nk - a.last_q - kb * KB + dl - o_min] += ds;
+      }
+    }
   }
-  float* pd = a.part_diag + (row * a.nchunks + c) * DSPAN;
-  for (int i = tid; i < DSPAN; i += 256) pd[i] = s_diag[i];
+  if (col_pend >= 0) vo[col_pend] = cs_pend;
+  __syncthreads();
+  if (gi.on) {
+    float* pd = a.part_diag + (row * a.nchunks + c) * DSPAN;
+    for (int i = tl; i < DSPAN; i += 128) pd[i] = s_diag[g][i];
+  }
 }
 
 __global__ __launch_bounds__(256) void vs_diag_combine_kernel(VsScoreArgs a) {
@@ -269,9 +320,30 @@ hipError_t launch_vs_scores(const VsScoreArgs& a0, hipStream_t st) {
   VsScoreArgs a = a0;
   a.chunk_tiles = CH;
   a.nchunks = ((a.Nk + 63) / 64 + CH - 1) / CH;
-  dim3 grid(a.heads.n, a.nchunks, a.B);
-  hipLaunchKernelGGL(vs_pass1_kernel, grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(vs_pass2_kernel, grid, dim3(256), 0, st, a);
+  // listed heads grouped by KV head (stable), split into groups of at most GH
+  VsGroupTable t;
+  t.n = 0;
+  int pos = 0;
+  const int rep = a.H / a.Hkv;
+  bool done[256] = {};
+  for (int i = 0; i < a.heads.n; ++i) {
+    if (done[i]) continue;
+    const int kvh = a.heads.h[i] / rep;
+    for (int j = i; j < a.heads.n; ++j) {
+      if (done[j] || a.heads.h[j] / rep != kvh) continue;
+      if (t.n == 0 || t.cnt[t.n - 1] == GH || a.heads.h[t.order[t.first[t.n - 1]]] / rep != kvh) {
+        t.first[t.n] = (int16_t)pos;
+        t.cnt[t.n] = 0;
+        ++t.n;
+      }
+      t.order[pos++] = (int16_t)j;
+      ++t.cnt[t.n - 1];
+      done[j] = true;
+    }
+  }
+  dim3 grid(t.n, a.nchunks, a.B);
+  hipLaunchKernelGGL(vs_group_pass1_kernel, grid, dim3(GT), 0, st, a, t);
+  hipLaunchKernelGGL(vs_group_pass2_kernel, grid, dim3(GT), 0, st, a, t);
   const int cb = std::min(64, (a.Nk + 255) / 256);
   hipLaunchKernelGGL(vs_diag_combine_kernel, dim3(cb, a.heads.n, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
