@@ -382,6 +382,13 @@ constexpr int OFF_COLS = 2 * 2 * TK * 256;         // after the 64-key ring [sta
 constexpr int OFF_COV = OFF_COLS + GCAP * 4;
 constexpr int OFF_MISC = OFF_COV + GCAP;
 static_assert(OFF_MISC + 8 * 4 <= LDS_BYTES, "LDS arena overflow");
+// Small-block gather (blocks of 16 or 32): a two-stage ring of 32-key units
+// (two slots), then a 16-bit mask per unit and the compacted unit list; the
+// shared counters at OFF_MISC stay clear of both.
+constexpr int kSmallUnits = 7168;                  // 32-key units per item (keys < 229376)
+constexpr int OFF_UMASK = 2 * SLOT;
+constexpr int OFF_ULIST = OFF_UMASK + kSmallUnits * 2;
+static_assert(OFF_ULIST + kSmallUnits * 4 <= OFF_MISC, "small-block regions overlap the shared counters");
 
 __device__ __forceinline__ int mod5(int u) { return ((u % NSLOT) + NSLOT) % NSLOT; }
 
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       // bf16 weights exp2(s scale - muse) of one sub-block (the row sum takes
       // the same rounded values), then O^T += V^T P^T with the V rows at vofs
       // (two 16-key steps).
-      auto pv32 = [&](const f32x16& sacc, float muse, uint32_t vofs) {
+      auto pv32 = [&](const f32x16& sacc, float muse, uint32_t vofs, uint32_t halves = 3u) {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         uint32_t pk[8];
 #pragma unroll
@@ -556,6 +563,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+          // a 16-key half no lane of the wave kept has only zero weights: its
+          // product adds nothing (halves: bit s2 set when some lane keeps one)
+          if (!((halves >> s2) & 1u)) continue;
           u32x4 bx = {pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
           const bf16x8 bop = __builtin_bit_cast(bf16x8, bx);
           // rows 16 s2 + v_row0 (a) and + 8 (b): the same swizzle as row v_row0
@@ -586,8 +596,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         f32x16 sacc;
         qk32(kofs, sacc);
         if (__builtin_amdgcn_ballot_w64(M != ~0u) != 0) mask32(sacc, M);
+        const uint32_t halves = (__builtin_amdgcn_ballot_w64((M & 0xFFFFu) != 0u) != 0 ? 1u : 0u) |
+                                (__builtin_amdgcn_ballot_w64((M >> 16) != 0u) != 0 ? 2u : 0u);
         const float muse = grow_to(lane_max(sacc));
-        pv32(sacc, muse, vofs);
+        pv32(sacc, muse, vofs, halves);
       };
 
       // Two 32x32 sub-blocks of one 64-key tile (the second at + 32 rows): both
@@ -743,11 +755,93 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
         }
         __syncthreads();                         // the slots are free for the gather phase
+      } else if (SMALL && it.kind == 2 && a.block < TK && it.last_pos / 32 < kSmallUnits) {
+        // Blocks of 16 or 32, gathered per item: the item's query blocks (8 of
+        // 16 rows or 4 of 32) mark the 16-key halves of every 32-key unit they
+        // selected in a per-unit mask (16 bits: query block q, half h at bit
+        // 2 q + h); the marked units are compacted into one ascending list and
+        // streamed through a two-stage ring, each unit's K and V loaded once for
+        // all four waves.  A wave computes a unit for the rows of its query
+        // blocks that selected it (its mask bits, and causal), so the softmax of
+        // every row is merged on chip across the units it uses.
+        __syncthreads();                         // every wave has read the item number; the arena is free
+        const int nu = it.last_pos / 32 + 1;     // 32-key units the item's rows can see
+        uint16_t* const umask = (uint16_t*)(s_lds + OFF_UMASK);
+        uint32_t* const ulist = (uint32_t*)(s_lds + OFF_ULIST);
+        uint32_t* const umask32 = (uint32_t*)umask;
+        for (int i = tid; i < (nu + 1) / 2; i += NT) umask32[i] = 0u;
+        __syncthreads();
+        {
+          const int sh = a.block == 16 ? 1 : 0;  // list entry J lies in unit J >> sh
+          const int nq_item = 2 * TQ / a.block;
+          const int I0 = it.P0 / a.block;
+          for (int q = w; q < nq_item; q += 4) {
+            const int I = I0 + q;
+            if (I >= a.nqb || I * a.block > it.last_pos) continue;
+            const int32_t* li = a.bidx + ((size_t)it.bh * a.nqb + I) * a.bcap;
+            const int n = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I), a.bcap);
+            for (int x = l; x < n; x += 64) {
+              const int J = li[x];
+              const int u = J >> sh;
+              if (J < 0 || u >= nu) continue;   // out of range, or after the item's last row
+              const uint32_t bits = sh ? (1u << (2 * q + (J & 1))) : (3u << (2 * q));
+              atomicOr(&umask32[u >> 1], bits << (16 * (u & 1)));
+            }
+          }
+        }
+        __syncthreads();
+        int nlist = 0;
+        for (int u0 = 0; u0 < nu; u0 += NT) {
+          const int u = u0 + tid;
+          const uint32_t m = u < nu ? (uint32_t)umask[u] : 0u;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(m != 0u);
+          if (l == 0) s_misc[1 + w] = __popcll(bal);
+          __syncthreads();
+          int off = nlist;
+          for (int i = 0; i < w; ++i) off += s_misc[1 + i];
+          if (m != 0u) ulist[off + ballot_rank(bal)] = (uint32_t)u | (m << 16);
+          nlist += s_misc[1] + s_misc[2] + s_misc[3] + s_misc[4];
+          __syncthreads();
+        }
+        auto issue_unit = [&](int u, uint32_t lb) {
+          const int k0 = 32 * u;
+          if (k0 + 32 <= a.Nk) {
+            const char* kb = (const char*)(kbp + (size_t)k0 * 128);
+            const char* vb = (const char*)(vbp + (size_t)k0 * 128);
+            dma16x4(kb + off_k, kb + off_k + 4096, vb + off_v, vb + off_v + 4096, lb + w * 1024,
+                    lb + (4 + w) * 1024, lb + 8192 + w * 1024, lb + 8192 + (4 + w) * 1024);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int r = 16 * j + rl;
+              const int key = min(k0 + r, a.Nk - 1);
+              dma16(kbp + (size_t)key * 128 + swz_k(r, l & 15) * 8, lb + (4 * j + w) * 1024);
+              dma16(vbp + (size_t)key * 128 + swz_v(r, l & 15) * 8, lb + 8192 + (4 * j + w) * 1024);
+            }
+          }
+        };
+        if (nlist > 0) issue_unit((int)(ulist[0] & 0xFFFFu), ring);
+        take_q();
+        // this lane's query block within the item and the shift of its mask bits
+        const int qsh = 2 * ((32 * w + qn) / a.block);
+        for (int i = 0; i < nlist; ++i) {
+          const uint32_t e = ulist[i];
+          wait_vm();
+          __syncthreads();                       // unit i landed; every wave is done with unit i - 1
+          if (i + 1 < nlist) issue_unit((int)(ulist[i + 1] & 0xFFFFu), ring + (uint32_t)(((i + 1) & 1) * SLOT));
+          const int u = (int)(e & 0xFFFFu);
+          const uint32_t g = (e >> (16 + qsh)) & 3u;
+          uint32_t M = ((g & 1u) ? 0x0000FFFFu : 0u) | ((g & 2u) ? 0xFFFF0000u : 0u);
+          M &= causal_mask32(iq - 32 * u);
+          const uint32_t st = (uint32_t)((i & 1) * SLOT);
+          sub32(st, st + 8192, M);
+        }
+        it.kind = 4;                             // no tile steps for this item
       } else if (SMALL && it.kind == 2 && a.block < TK) {
-        // Blocks of 16 or 32: each wave walks the lists of its own 32 rows (one
-        // list for block 32, two for block 16) 32 keys at a time through its
-        // own 16 KB slot of the arena, with no workgroup barrier: the pair's
-        // waves share no key blocks worth a joint step.
+        // Blocks of 16 or 32 on very long sequences (more 32-key units than the
+        // gather masks hold): each wave walks the lists of its own 32 rows (one
+        // list for block 32, two for block 16) 32 keys at a time through its own
+        // 16 KB slot of the arena, with no workgroup barrier.
         __syncthreads();                         // every wave has read the item number
         const uint32_t wslot = (uint32_t)(w * SLOT);
         if (R0w <= it.last_pos) {
