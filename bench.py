@@ -52,6 +52,8 @@ WORKLOADS = {
                          "pooled block scores (block 64: 16 key blocks, 32 block offsets)",
                          lambda: synth.config(3, vs_rule="pooled")),
     "vs4k": ("one Vertical-Slash head, N=4096, last_q 64, 256 cols + 256 diags", lambda: synth.config(1)),
+    "dense32k": ("dense causal attention, 32 Q / 8 KV heads, d=128, N=32768 (every key of every row selected)",
+                 lambda: synth.dense_layer()),
     "block32k-topk": ("8 block heads, N=32768, block 64, top-16 + first + diagonal", lambda: synth.config(2)),
     "block32k-thresh": ("8 block heads, N=32768, block 64, threshold max - ln 20 + first + diagonal",
                         lambda: synth.config(2, mode="thresh")),
@@ -83,6 +85,8 @@ def selected_count_layer(layer, w):
     for b in range(B):
         for h in range(H):
             kind = layer.kinds[h]
+            if kind == dsa.TOKEN:
+                continue                  # token heads are counted from their token lists by the caller
             if kind == dsa.DENSE:
                 total += int((pos + 1).sum())
             elif kind == dsa.VS:
@@ -117,6 +121,19 @@ def _oracle_threads():
     except Exception:
         pass
     return threads
+
+
+def _host_cpu():
+    """nproc and the CPU model of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return os.cpu_count(), model
 
 
 def cpu_baseline(w, sample_rows=512, seed=0):
@@ -402,6 +419,39 @@ def vs_compare(args, dev, stream):
     print(json.dumps(rec), flush=True)
 
 
+def attn_kind(args, dev, stream):
+    """The attention launch of the headline layer for the heads of one pattern
+    kind only, through the public ABI: the layer's index sets are built as
+    usual, then sparse_prefill_attn runs with the other heads as token heads
+    with empty lists (handled by a separate kernel), so the attention kernel's
+    launch covers exactly that kind.  One JSON line: ms, selected FLOPs, rate."""
+    w = synth.config(3)
+    B, H, Hkv, Nq, Nk, d = w.shape
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
+    layer.build_indices(q, k)
+    pick = {"ashape": lambda p: p.kind == dsa.VS and p.ashape,
+            "vs": lambda p: p.kind == dsa.VS and not p.ashape,
+            "block": lambda p: p.kind == dsa.BLOCK}[args.attn_kind]
+    heads = [h for h, p in enumerate(w.heads) if pick(p)]
+    kinds = [layer.kinds[h] if h in heads else dsa.TOKEN for h in range(H)]
+    tok = dsa.TokenIndex.empty(B, Nq, 1, dev)                    # empty lists
+    attn = lambda: dsa.sparse_prefill_attn(q, k, v, kinds, vs=layer.vs_index, blk=layer.blk_index, tok=tok,
+                                           out_dtype=dsa.OUT_BF16, o=layer.o, lse=layer.lse, ws=layer.ws)
+    ms, _, _ = time_steps([attn], args.steps, args.warmup, stream)
+    sub = synth.Workload(w.name, w.q, w.k, w.v, w.heads, w.q_offset, w.extra)
+    f_all = 4 * d * selected_count_layer(layer, sub)
+    kinds_saved = layer.kinds
+    layer.kinds = [kinds_saved[h] if h in heads else dsa.TOKEN for h in range(H)]
+    f_sel = 4 * d * selected_count_layer(layer, sub)
+    layer.kinds = kinds_saved
+    rec = {"metric": f"attention launch of the 128K mixed layer's {args.attn_kind} heads only", "unit": "TFLOP/s",
+           "value": round(f_sel / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4), "heads": heads, "f_sel": f_sel,
+           "f_sel_layer": f_all, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": WORKLOADS["mixed128k"][0], "name": f"mixed128k-{args.attn_kind}"}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +466,8 @@ def main():
     ap.add_argument("--vs-compare", action="store_true",
                     help="only compare Vertical-Slash discovery by last_q scoring and by pooled block scores on the "
                          "128K mixed layer (time, recall, output against dense) and exit")
+    ap.add_argument("--attn-kind", choices=["ashape", "vs", "block"],
+                    help="only time the attention launch of the 128K mixed layer for the heads of one kind and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -432,6 +484,9 @@ def main():
         return
     if args.vs_compare:
         vs_compare(args, dev, torch.cuda.current_stream(dev))
+        return
+    if args.attn_kind:
+        attn_kind(args, dev, torch.cuda.current_stream(dev))
         return
     desc, make = WORKLOADS[args.workload]
     log(f"[bench] generating {args.workload}")
@@ -542,10 +597,14 @@ def main():
         log("[bench] timing the CPU oracle on a sample")
         cb = cpu_baseline_indexer(w) if args.workload.startswith("indexer") else cpu_baseline(w)
         t_cpu = cb["t_index"] + cb["t_attn_layer"]
+        nproc, model = _host_cpu()
         rec["cpu_baseline"] = {
             "value": round(f_sel / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cb["threads"], "kind": "oracle",
+            "nproc": nproc, "cpu_model": model,
             "sample": f"fp64 numpy oracle, {cb['sample']}; t_index {cb['t_index']:.2f}s, attention sample "
-                      f"{cb['t_attn_sample']:.2f}s, layer estimate {t_cpu:.1f}s ({t_cpu * 1e3:.0f} ms per layer)",
+                      f"{cb['t_attn_sample']:.2f}s, layer estimate {t_cpu:.1f}s ({t_cpu * 1e3:.0f} ms per layer); "
+                      f"BLAS and torch use {cb['threads']} threads (the process's thread setting, "
+                      f"OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', 'unset')}) of the host's {nproc}",
         }
     print(json.dumps(rec), flush=True)
 

@@ -301,6 +301,13 @@ def indexer_chunk(seed: int = 5, N: int = 131072, Nq: int = 8192, Hi: int = 64, 
                            "route_heads": route_heads, "route_block": 64, "cand": cand})
 
 
+def dense_layer(seed: int = 7, N: int = 32768, H: int = 32, Hkv: int = 8) -> Workload:
+    """Q, K, V ~ N(0, 1), every head dense causal: the all-selected special case."""
+    g = _gen(seed)
+    q, k, v = _bf(*_qkv(g, 1, H, Hkv, N))
+    return Workload(f"dense_N{N}", q, k, v, [HeadPlan(DENSE) for _ in range(H)])
+
+
 def config(c: int, **kw) -> Workload:
     """The five workloads at their stated sizes (keyword arguments shrink them)."""
     if c == 1:
