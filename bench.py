@@ -420,34 +420,31 @@ def vs_compare(args, dev, stream):
 
 
 def attn_kind(args, dev, stream):
-    """The attention launch of the headline layer for the heads of one pattern
-    kind only, through the public ABI: the layer's index sets are built as
-    usual, then sparse_prefill_attn runs with the other heads as token heads
-    with empty lists (handled by a separate kernel), so the attention kernel's
-    launch covers exactly that kind.  One JSON line: ms, selected FLOPs, rate."""
+    """One pattern kind of the headline layer on its own, through the public
+    ABI: a layer of the 128K mixed workload's heads of three or four whole KV
+    groups, every head given that kind's plan (A-shape: heads 0-11 on KV heads
+    0-2; Vertical-Slash: heads 12-27 on KV heads 3-6; block top-128 of 64:
+    heads 24-31 on KV heads 6-7), on those heads' own data.  Its index build
+    and attention are timed like a layer step.  One JSON line."""
     w = synth.config(3)
     B, H, Hkv, Nq, Nk, d = w.shape
-    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
-    layer = SparsePrefillLayer(w.heads, B, H, Hkv, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
-    layer.build_indices(q, k)
-    pick = {"ashape": lambda p: p.kind == dsa.VS and p.ashape,
-            "vs": lambda p: p.kind == dsa.VS and not p.ashape,
-            "block": lambda p: p.kind == dsa.BLOCK}[args.attn_kind]
-    heads = [h for h, p in enumerate(w.heads) if pick(p)]
-    kinds = [layer.kinds[h] if h in heads else dsa.TOKEN for h in range(H)]
-    tok = dsa.TokenIndex.empty(B, Nq, 1, dev)                    # empty lists
-    attn = lambda: dsa.sparse_prefill_attn(q, k, v, kinds, vs=layer.vs_index, blk=layer.blk_index, tok=tok,
-                                           out_dtype=dsa.OUT_BF16, o=layer.o, lse=layer.lse, ws=layer.ws)
-    ms, _, _ = time_steps([attn], args.steps, args.warmup, stream)
-    sub = synth.Workload(w.name, w.q, w.k, w.v, w.heads, w.q_offset, w.extra)
-    f_all = 4 * d * selected_count_layer(layer, sub)
-    kinds_saved = layer.kinds
-    layer.kinds = [kinds_saved[h] if h in heads else dsa.TOKEN for h in range(H)]
+    rep = H // Hkv
+    span = {"ashape": (0, 12), "vs": (12, 28), "block": (24, 32)}[args.attn_kind]
+    plan_of = {"ashape": w.heads[0], "vs": w.heads[12], "block": w.heads[31]}[args.attn_kind]
+    h0, h1 = span
+    q = w.q[:, h0:h1].contiguous().to(dev)
+    k = w.k[:, h0 // rep:h1 // rep].contiguous().to(dev)
+    v = w.v[:, h0 // rep:h1 // rep].contiguous().to(dev)
+    sub = synth.Workload(f"{w.name}-{args.attn_kind}", q, k, v, [plan_of] * (h1 - h0), w.q_offset, w.extra)
+    Hs, Hkvs = h1 - h0, (h1 - h0) // rep
+    layer = SparsePrefillLayer(sub.heads, B, Hs, Hkvs, Nk, dev, out_dtype=dsa.OUT_BF16, want_lse=True)
+    phases = [lambda: layer.build_indices(q, k), lambda: layer.attention(q, k, v)]
+    ms_step, (ms_index, ms_attn), _ = time_steps(phases, args.steps, args.warmup, stream)
     f_sel = 4 * d * selected_count_layer(layer, sub)
-    layer.kinds = kinds_saved
-    rec = {"metric": f"attention launch of the 128K mixed layer's {args.attn_kind} heads only", "unit": "TFLOP/s",
-           "value": round(f_sel / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4), "heads": heads, "f_sel": f_sel,
-           "f_sel_layer": f_all, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+    rec = {"metric": f"attention of the 128K mixed layer's data, {args.attn_kind} heads only", "unit": "TFLOP/s",
+           "value": round(f_sel / (ms_attn * 1e-3) / 1e12, 2), "ms_attn": round(ms_attn, 4),
+           "ms_index": round(ms_index, 4), "heads": list(range(h0, h1)), "kv_heads": list(range(h0 // rep, h1 // rep)),
+           "f_sel": f_sel, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
            "data": "synthetic", "config": {"workload": WORKLOADS["mixed128k"][0], "name": f"mixed128k-{args.attn_kind}"}}
     print(json.dumps(rec), flush=True)
 
@@ -467,7 +464,7 @@ def main():
                     help="only compare Vertical-Slash discovery by last_q scoring and by pooled block scores on the "
                          "128K mixed layer (time, recall, output against dense) and exit")
     ap.add_argument("--attn-kind", choices=["ashape", "vs", "block"],
-                    help="only time the attention launch of the 128K mixed layer for the heads of one kind and exit")
+                    help="only time a layer of one pattern kind on the 128K mixed layer's data and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
