@@ -212,9 +212,10 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k, 
   WsCarver c(ws);
   float* vbuf = c.take<float>(R * Nk);
   float* sbuf = c.take<float>(R * Nk);
-  const int nchunks = (int)(((Nk + 63) / 64 + 15) / 16);
-  float* pml = c.take<float>(R * nchunks * 128);
-  float* pdg = c.take<float>(R * nchunks * (16 * 64 + 64));
+  size_t n_ml, n_dg;
+  vs_part_floats((int)R, (int)Nk, &n_ml, &n_dg);
+  float* pml = c.take<float>(n_ml);
+  float* pdg = c.take<float>(n_dg);
   VsScoreArgs a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -225,8 +226,6 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k, 
   a.s_out = s_scores ? s_scores : sbuf;
   a.part_ml = pml;
   a.part_diag = pdg;
-  a.nchunks = nchunks;
-  a.chunk_tiles = 16;
   hipStream_t s = (hipStream_t)stream;
   if ((st = hip_status(launch_vs_scores(a, s), "build_index_vs: scores"))) return st;
   return hip_status(launch_vs_select(a.v_out, a.s_out, shape->batch, shape->kv_len, shape->heads, hl, nv, ns, out.cols,

@@ -186,22 +186,6 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
-// 16 bytes per lane straight from global memory into LDS; lane l of the wave
-// lands at LDS byte address lds_addr + 16 l (lds_addr is wave-uniform).
-// Issued from inline assembly on purpose: the compiler does not track these
-// LDS writes, so it adds no wait of its own before the LDS reads of the other
-// ring stage (its own wait would drain the DMA just issued for the next tile).
-// The explicit vmcnt wait at the top of each step orders a tile's DMA before
-// the reads of its stage; the "memory" clobber keeps the compiler from moving
-// LDS accesses across the issue.  The instruction has no register results.
-// M0 (the LDS base) is saved and restored around it, so the compiler's view of
-// M0 never changes.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(save) : "v"(g), "s"(lds_addr) : "memory");
-}
 // Four DMAs of 1 KB (a full tile's share of one wave) with one M0 save/restore.
 __device__ __forceinline__ void dma16x4(const char* g0, const char* g1, const char* g2, const char* g3, uint32_t l0,
                                         uint32_t l1, uint32_t l2, uint32_t l3) {

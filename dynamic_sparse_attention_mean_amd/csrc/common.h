@@ -95,4 +95,23 @@ __device__ __forceinline__ uint32_t ballot_rank(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// ---------------------------------------------------------------------------
+// 16 bytes per lane straight from global memory into LDS; lane l of the wave
+// lands at LDS byte address lds_addr + 16 l (lds_addr is wave-uniform).
+// Issued from inline assembly on purpose: the compiler does not track these
+// LDS writes, so it adds no wait of its own before LDS reads or writes that it
+// cannot tell apart from the DMA's target (its own wait would drain the DMA
+// just issued for a later stage of a ring).  The caller orders a DMA before
+// the reads of its stage with an explicit vmcnt wait; the "memory" clobber
+// keeps the compiler from moving LDS accesses across the issue.  The
+// instruction has no register results.  M0 (the LDS base) is saved and
+// restored around it, so the compiler's view of M0 never changes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(g), "s"(lds_addr) : "memory");
+}
+
 }  // namespace dsa

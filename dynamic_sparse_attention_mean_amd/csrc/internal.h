@@ -74,7 +74,8 @@ struct VsScoreArgs {
   float* s_out;           // [B, n_heads, Nk] diagonal sums
   float* part_ml;         // [B, n_heads, nchunks, 2, 64] per-chunk row max / sum
   float* part_diag;       // [B, n_heads, nchunks, chunk_keys + 64] per-chunk diagonal sums
-  int nchunks, chunk_tiles;
+  float* row_stats;       // [B, n_heads, 2, 64] each row's maximum and 1 / sum (after part_ml)
+  int nchunks, chunk_keys; // set by launch_vs_scores
 };
 // Listed heads grouped by KV head for the scoring passes: group s holds the
 // listed indices order[first[s] .. first[s] + cnt[s]) (at most 4, one KV head).
@@ -85,6 +86,7 @@ struct VsGroupTable {
   int8_t cnt[256];
 };
 size_t vs_workspace_floats(int n_rows, int Nk);   // n_rows = B * n_heads
+void vs_part_floats(int n_rows, int Nk, size_t* ml, size_t* diag);   // the per-chunk partials within it
 hipError_t launch_vs_scores(const VsScoreArgs& a, hipStream_t st);
 
 // Top-nv of v and top-ns of s per listed head ([B, n_heads, Nk] rows) into the

@@ -17,12 +17,17 @@
 #include "internal.h"
 #include "select.h"
 
+#include <algorithm>
+
 namespace dsa {
 namespace {
 
-constexpr int CH = 16;           // key tiles per chunk
-constexpr int CK = CH * 64;      // keys per chunk
-constexpr int DSPAN = CK + 64;   // diagonal partials per chunk (CK + 63 used)
+// A chunk of keys (one workgroup per group of heads and chunk) holds a multiple
+// of 32 keys, at most kVsChunkMax; the host picks the size that spreads the
+// workgroups most evenly over the chip.  Pass 2 keeps a chunk's column sums and
+// diagonal partials (chunk + 63 of them) in LDS.
+constexpr int kVsChunkMin = 256;
+constexpr int kVsChunkMax = 512;
 
 struct Frag {
   bf16x8 q[8];
@@ -52,12 +57,10 @@ constexpr float kScale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(
 constexpr int GH = 4;                // heads per workgroup
 constexpr int GT = 2 * GH * 64;      // threads: wave w serves head slot w / 2, rows 32 (w % 2) ..
 constexpr int KB = 32;               // keys per block
-constexpr int CKB = CK / KB;         // blocks per chunk
 
-typedef __attribute__((address_space(3))) void lds_void_vs_t;
+typedef __attribute__((address_space(3))) char lds_char_vs_t;
 __device__ __forceinline__ void vs_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int vs_swz(int r, int c) { return c ^ (r & 15); }
-
 // DMA of K block kb (32 keys, 8 KB) into an LDS stage: lane l of wave w takes
 // row 4 w + l / 16 and writes LDS chunk l % 16 of that row, which holds the
 // row's 16-byte chunk (l % 16) ^ (row % 16); keys past the end are clamped.
@@ -66,7 +69,15 @@ __device__ __forceinline__ void vs_issue_block(const uint16_t* kp, int Nk, int k
   const int r = 4 * w + (l >> 4);
   const int key = min(kb * KB + r, Nk - 1);
   const int c = vs_swz(r, l & 15);
-  __builtin_amdgcn_global_load_lds(kp + (size_t)key * 128 + c * 8, (lds_void_vs_t*)(stage + w * 1024), 16, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_vs_t*)stage + w * 1024);
+  dma16(kp + (size_t)key * 128 + c * 8, lds);
+}
+// The compiler's wait for the Q fragment loads, placed here (after the first
+// DMAs are issued) rather than at their first use inside a block loop, where
+// it would drain the DMAs of later blocks in every iteration.
+__device__ __forceinline__ void vs_take_q(const Frag& f) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" :: "v"(f.q[ks]));
 }
 
 // S^T of one 32-key block against this wave's 32 query rows, K from LDS.
@@ -100,14 +111,17 @@ __device__ __forceinline__ VsGroupInfo vs_group_info(const VsScoreArgs& a, const
   return gi;
 }
 
-// Wait until at most n of this wave's DMAs are outstanding (n = 0, 1, 2).
+// Wait until at most n of this wave's DMAs are outstanding (n = 0 .. 4).
 __device__ __forceinline__ void vs_wait_vm_upto(int n) {
-  if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-constexpr int P1ST = 4;              // pass 1 ring stages: blocks prefetched three ahead
+constexpr int P1ST = 6;              // pass 1 ring stages: blocks prefetched five ahead
+constexpr int P2ST = 3;              // pass 2 ring stages: blocks prefetched two ahead
 
 __global__ __launch_bounds__(GT) void vs_group_pass1_kernel(VsScoreArgs a, VsGroupTable t) {
   __shared__ __align__(1024) char s_k[P1ST][KB * 256];
@@ -120,15 +134,17 @@ __global__ __launch_bounds__(GT) void vs_group_pass1_kernel(VsScoreArgs a, VsGro
   load_qfrag(a, b, gi.h, gi.on ? r : 64, f);           // rows >= last_q load zeros
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + gi.kvh) * a.Nk) * 128;
   const int nblk = (a.Nk + KB - 1) / KB;
-  const int kb0 = c * CKB, kb1 = min(nblk, kb0 + CKB);
+  const int cb = a.chunk_keys / KB;
+  const int kb0 = c * cb, kb1 = min(nblk, kb0 + cb);
   float m = -INFINITY, s = 0.f;
   // the loop stores nothing, so DMAs are this wave's only vector memory
   // operations and complete in issue order: a partial count is safe
   for (int i = 0; i < P1ST - 1 && kb0 + i < kb1; ++i) vs_issue_block(kp, a.Nk, kb0 + i, s_k[i]);
+  vs_take_q(f);
   for (int kb = kb0; kb < kb1; ++kb) {
     const int st = (kb - kb0) % P1ST;
     vs_wait_vm_upto(min(P1ST - 2, kb1 - 1 - kb));     // block kb landed (later ones may be in flight)
-    __syncthreads();                                  // ... for every wave; all are done with kb - 1
+    __syncthreads();                                 // ... for every wave; all are done with kb - 1
     if (kb + P1ST - 1 < kb1) vs_issue_block(kp, a.Nk, kb + P1ST - 1, s_k[(st + P1ST - 1) % P1ST]);
     if (gi.on) {
       const f32x16 acc = vs_block_scores(s_k[st], f);
@@ -164,12 +180,60 @@ __global__ __launch_bounds__(GT) void vs_group_pass1_kernel(VsScoreArgs a, VsGro
   }
 }
 
+// Each row's maximum and sum over all chunks of pass 1: sixteen threads per row
+// merge contiguous runs of chunks (ascending), then one merges the sixteen
+// results in order.  Writes the maximum and 1 / sum.
+__global__ __launch_bounds__(1024) void vs_row_stats_kernel(VsScoreArgs a) {
+  __shared__ float s_m[16][64], s_s[16][64];
+  const int hi = blockIdx.x, b = blockIdx.y;
+  const size_t row = (size_t)(b * a.heads.n + hi);
+  const int r = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int per = (a.nchunks + 15) / 16;
+  const int c0 = min(a.nchunks, p * per), c1 = min(a.nchunks, c0 + per);
+  const float* pm = a.part_ml + (row * a.nchunks) * 128;
+  float m = -INFINITY, s = 0.f;
+  for (int cb = c0; cb < c1; cb += 8) {
+    float mc[8], sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {               // eight chunks' loads in flight
+      const bool ok = cb + j < c1;
+      mc[j] = ok ? pm[(size_t)(cb + j) * 128 + r] : -INFINITY;
+      sc[j] = ok ? pm[(size_t)(cb + j) * 128 + 64 + r] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float mn = fmaxf(m, mc[j]);
+      if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m - mn) + sc[j] * __builtin_amdgcn_exp2f(mc[j] - mn);
+      m = mn;
+    }
+  }
+  s_m[p][r] = m;
+  s_s[p][r] = s;
+  __syncthreads();
+  if (p == 0) {
+    m = -INFINITY;
+    s = 0.f;
+    for (int q = 0; q < 16; ++q) {
+      const float mq = s_m[q][r], sq = s_s[q][r];
+      const float mn = fmaxf(m, mq);
+      if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m - mn) + sq * __builtin_amdgcn_exp2f(mq - mn);
+      m = mn;
+    }
+    a.row_stats[row * 128 + r] = m;
+    a.row_stats[row * 128 + 64 + r] = s > 0.f ? 1.0f / s : 0.f;
+  }
+}
+
+// Pass 2.  The loop issues no global stores (a store shares the DMA's counter
+// and would make the partial waits unsafe): a chunk's column sums and diagonal
+// partials collect in LDS and are written out once at the end.
 __global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGroupTable t) {
-  __shared__ __align__(1024) char s_k[2][KB * 256];
+  __shared__ __align__(1024) char s_k[P2ST][KB * 256];
   __shared__ float s_p[GH][64 * (KB + 1)];
-  __shared__ float s_diag[GH][DSPAN];
+  __shared__ float s_diag[GH][kVsChunkMax + 64];
+  __shared__ float s_col[GH][kVsChunkMax];
   __shared__ float s_mr[GH][64], s_il[GH][64];
-  const int c = blockIdx.y, b = blockIdx.z;
+  const int CK = a.chunk_keys, c = blockIdx.y, b = blockIdx.z;
   const VsGroupInfo gi = vs_group_info(a, t);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hh = l >> 5, qn = l & 31;
   const int g = w >> 1;
@@ -177,44 +241,30 @@ __global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGro
   const int pr = a.Nk - a.last_q + r;
   const size_t row = (size_t)(b * a.heads.n + gi.hi);
 
-  // final row max and sum of each head, over all chunks in ascending order
+  // each row's final maximum and 1 / sum (vs_row_stats_kernel)
   if ((w & 1) == 0 && gi.on) {
-    const float* pm = a.part_ml + (row * a.nchunks) * 128;
-    float m = -INFINITY, s = 0.f;
-    for (int cc = 0; cc < a.nchunks; ++cc) {
-      const float mc = pm[cc * 128 + l], sc = pm[cc * 128 + 64 + l];
-      const float mn = fmaxf(m, mc);
-      if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m - mn) + sc * __builtin_amdgcn_exp2f(mc - mn);
-      m = mn;
-    }
-    s_mr[g][l] = m;
-    s_il[g][l] = s > 0.f ? 1.0f / s : 0.f;
+    s_mr[g][l] = a.row_stats[row * 128 + l];
+    s_il[g][l] = a.row_stats[row * 128 + 64 + l];
   }
-  for (int i = tid; i < GH * DSPAN; i += GT) (&s_diag[0][0])[i] = 0.f;
+  for (int i = tid; i < GH * (kVsChunkMax + 64); i += GT) (&s_diag[0][0])[i] = 0.f;
   Frag f;
   load_qfrag(a, b, gi.h, gi.on ? r : 64, f);
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + gi.kvh) * a.Nk) * 128;
   const int nblk = (a.Nk + KB - 1) / KB;
-  const int kb0 = c * CKB, kb1 = min(nblk, kb0 + CKB);
+  const int kb0 = c * (CK / KB), kb1 = min(nblk, kb0 + CK / KB);
   const int o_min = a.Nk - a.last_q - (c + 1) * CK + 1;   // offset of diagonal slot 0 of this chunk
-  float* vo = a.v_out + row * a.Nk;
   float* sp = s_p[g];
   const int tl = tid & 127;                               // this thread's place among its head's 128
-  vs_issue_block(kp, a.Nk, kb0, s_k[0]);
-  __syncthreads();                                        // row statistics visible
+  __syncthreads();                                        // row statistics visible; s_diag cleared
   const float mr = s_mr[g][r & 63], il = s_il[g][r & 63];
-  // A block's column sums are stored at the start of the next block, right
-  // after its wait: stores and the DMA share one counter, so a store issued at
-  // the end of a block would hold up the next block's wait for the DMA.
-  float cs_pend = 0.f;
-  int col_pend = -1;
+  // from here on the DMAs are the only vector memory operations in flight
+  for (int i = 0; i < P2ST - 1 && kb0 + i < kb1; ++i) vs_issue_block(kp, a.Nk, kb0 + i, s_k[i]);
+  vs_take_q(f);
   for (int kb = kb0; kb < kb1; ++kb) {
-    const int st = (kb - kb0) & 1;
-    vs_wait_vm();
-    __syncthreads();                                      // block kb landed; the last block's sums are done
-    if (col_pend >= 0) vo[col_pend] = cs_pend;
-    col_pend = -1;
-    if (kb + 1 < kb1) vs_issue_block(kp, a.Nk, kb + 1, s_k[st ^ 1]);
+    const int st = (kb - kb0) % P2ST;
+    vs_wait_vm_upto(min(P2ST - 2, kb1 - 1 - kb));         // block kb landed (later ones may be in flight)
+    __syncthreads();                                     // ... for every wave; the last block's sums are done
+    if (kb + P2ST - 1 < kb1) vs_issue_block(kp, a.Nk, kb + P2ST - 1, s_k[(st + P2ST - 1) % P2ST]);
     if (gi.on) {
       const f32x16 acc = vs_block_scores(s_k[st], f);
 #pragma unroll
@@ -235,7 +285,7 @@ __global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGro
         for (int i = 0; i < 16; ++i) cs += sp[(16 * part + i) * (KB + 1) + col];
         cs += __shfl_xor(cs, 1, 64);
         cs += __shfl_xor(cs, 2, 64);
-        if (part == 0 && kb * KB + col < a.Nk) { cs_pend = cs; col_pend = kb * KB + col; }
+        if (part == 0) s_col[g][(kb - kb0) * KB + col] = cs;
       }
       if (tl < 95) {
         // diagonal dl = r - cc in [-31, 63]: the terms of keys cc = 0 .. 31 (rows
@@ -254,27 +304,32 @@ __global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGro
       }
     }
   }
-  if (col_pend >= 0) vo[col_pend] = cs_pend;
   __syncthreads();
   if (gi.on) {
-    float* pd = a.part_diag + (row * a.nchunks + c) * DSPAN;
-    for (int i = tl; i < DSPAN; i += 128) pd[i] = s_diag[g][i];
+    float* vo = a.v_out + row * a.Nk;
+    const int n = min(a.Nk, kb1 * KB) - kb0 * KB;
+    for (int i = tl; i < n; i += 128) vo[kb0 * KB + i] = s_col[g][i];
+    float* pd = a.part_diag + (row * a.nchunks + c) * (size_t)(CK + 64);
+    for (int i = tl; i < CK + 64; i += 128) pd[i] = s_diag[g][i];
   }
 }
 
 __global__ __launch_bounds__(256) void vs_diag_combine_kernel(VsScoreArgs a) {
   const int hi = blockIdx.y, b = blockIdx.z;
   const size_t row = (size_t)(b * a.heads.n + hi);
-  const float* pd = a.part_diag + row * a.nchunks * DSPAN;
+  const int CK = a.chunk_keys, span = CK + 64;
+  const float* pd = a.part_diag + row * a.nchunks * span;
   float* so = a.s_out + row * a.Nk;
   for (int o = blockIdx.x * 256 + threadIdx.x; o < a.Nk; o += gridDim.x * 256) {
+    // chunk c holds offsets [Nk - last_q - (c + 1) CK + 1, Nk - last_q - c CK + 63]:
+    // at most two chunks, summed in ascending order
     int chi = (a.Nk - a.last_q + 63 - o) / CK;
     chi = min(chi, a.nchunks - 1);
     float s = 0.f;
     for (int cc = max(0, chi - 1); cc <= chi; ++cc) {
-      const int o_min = a.Nk - a.last_q - (cc * CH + CH - 1) * 64 - 63;
+      const int o_min = a.Nk - a.last_q - (cc + 1) * CK + 1;
       const int idx = o - o_min;
-      if (idx >= 0 && idx < CK + 63) s += pd[(size_t)cc * DSPAN + idx];
+      if (idx >= 0 && idx < CK + 63) s += pd[(size_t)cc * span + idx];
     }
     so[o] = s;
   }
@@ -311,15 +366,58 @@ __global__ void ashape_fill_kernel(int H, HeadList heads, int ncols, int ndiags,
 
 }  // namespace
 
+// Per-chunk partials for n_rows listed heads, enough for any chunk size the
+// launch may pick (the smallest gives the most chunks).
+void vs_part_floats(int n_rows, int Nk, size_t* ml, size_t* diag) {
+  size_t nch = 0, span = 0;
+  for (int ck = kVsChunkMin; ck <= kVsChunkMax; ck += KB) {
+    const size_t n = (size_t)(Nk + ck - 1) / ck;
+    nch = std::max(nch, n);
+    span = std::max(span, n * (size_t)(ck + 64));
+  }
+  *ml = (size_t)n_rows * (nch + 1) * 128;      // + each row's final statistics
+  *diag = (size_t)n_rows * span;
+}
+
 size_t vs_workspace_floats(int n_rows, int Nk) {
-  const int nchunks = ((Nk + 63) / 64 + CH - 1) / CH;
-  return (size_t)n_rows * (2 * (size_t)Nk + (size_t)nchunks * 128 + (size_t)nchunks * DSPAN);
+  size_t ml, dg;
+  vs_part_floats(n_rows, Nk, &ml, &dg);
+  return (size_t)n_rows * 2 * (size_t)Nk + ml + dg;
+}
+
+// Workgroups of pass 2 that run at once on the current device.
+static int vs_slots() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, vs_group_pass2_kernel, GT, 0) != hipSuccess || per <= 0)
+      per = 1;
+    cached[dev] = cus * per;
+  }
+  return cached[dev];
+}
+
+// The chunk size (a multiple of 32 keys in [kVsChunkMin, kVsChunkMax]) that
+// minimises rounds of workgroups x (keys per workgroup + a fixed start-up cost
+// of about four blocks: the Q loads and the ring's first fill), the pass time
+// when every workgroup streams its chunk at the same rate.  Ties go to the
+// larger chunk.
+static int vs_chunk_keys(int units_per_chunk_row, int Nk, int slots) {
+  int best = kVsChunkMax;
+  long long best_cost = -1;
+  for (int ck = kVsChunkMax; ck >= kVsChunkMin; ck -= KB) {
+    const long long wgs = (long long)units_per_chunk_row * ((Nk + ck - 1) / ck);
+    const long long cost = ((wgs + slots - 1) / slots) * (ck + 4 * KB);
+    if (best_cost < 0 || cost < best_cost) { best = ck; best_cost = cost; }
+  }
+  return best;
 }
 
 hipError_t launch_vs_scores(const VsScoreArgs& a0, hipStream_t st) {
   VsScoreArgs a = a0;
-  a.chunk_tiles = CH;
-  a.nchunks = ((a.Nk + 63) / 64 + CH - 1) / CH;
   // listed heads grouped by KV head (stable), split into groups of at most GH
   VsGroupTable t;
   t.n = 0;
@@ -341,8 +439,12 @@ hipError_t launch_vs_scores(const VsScoreArgs& a0, hipStream_t st) {
       done[j] = true;
     }
   }
+  a.chunk_keys = vs_chunk_keys(t.n * a.B, a.Nk, vs_slots());
+  a.nchunks = (a.Nk + a.chunk_keys - 1) / a.chunk_keys;
   dim3 grid(t.n, a.nchunks, a.B);
+  a.row_stats = a.part_ml + (size_t)a.B * a.heads.n * a.nchunks * 128;
   hipLaunchKernelGGL(vs_group_pass1_kernel, grid, dim3(GT), 0, st, a, t);
+  hipLaunchKernelGGL(vs_row_stats_kernel, dim3(a.heads.n, a.B), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(vs_group_pass2_kernel, grid, dim3(GT), 0, st, a, t);
   const int cb = std::min(64, (a.Nk + 255) / 256);
   hipLaunchKernelGGL(vs_diag_combine_kernel, dim3(cb, a.heads.n, a.B), dim3(256), 0, st, a);

@@ -115,6 +115,29 @@ def test_vs_index_batch_and_chunk(B, H, Hkv, Nk, Nq, heads, last_q):
                 assert int(out.cols_count[b, h]) == 0 and int(out.diags_count[b, h]) == 0, "unlisted head written"
 
 
+def test_vs_index_many_groups():
+    """build_index_vs over every head of a GQA layer (batch 2, 32 Q / 8 KV
+    heads, heads listed in a scrambled order, a ragged key count): 64 groups
+    of heads, so the scoring passes take chunks of another size than the
+    smaller cases; v / s rows and sets of every (batch, head) against the oracle."""
+    B, H, Hkv, Nk, Nq, last_q = 2, 32, 8, 8192 + 37, 8192 + 37, 64
+    w = synth.vs_multi(seed=77, B=B, H=H, Hkv=Hkv, Nk=Nk, Nq=Nq, last_q=last_q)
+    q, k, _ = dev(w)
+    heads = [int(x) for x in np.random.default_rng(5).permutation(H)]
+    nv, ns = 100, 300
+    out = dsa.VSIndex.empty(B, H, nv, ns, DEV)
+    vsc = torch.zeros(B, H, Nk, device=DEV)
+    ssc = torch.zeros(B, H, Nk, device=DEV)
+    dsa.build_index_vs(q, k, heads, last_q, nv, ns, out, v_scores=vsc, s_scores=ssc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for t, h in enumerate(heads):
+            v, s = O.vs_scores(f64(w.q[b, h, Nq - last_q:]), f64(w.k[b, h // (H // Hkv)]))
+            assert_vs_scores_close(vsc[b, t].cpu().double().numpy(), v, last_q, f"b{b} h{h} v")
+            assert_vs_scores_close(ssc[b, t].cpu().double().numpy(), s, last_q, f"b{b} h{h} s")
+            check_vs_sets(out, b, h, v, s, nv, ns, f"b{b} h{h}")
+
+
 @pytest.mark.parametrize("block,mode", [(64, "topk"), (32, "thresh"), (128, "topk")])
 def test_block_index_batch2(block, mode):
     """build_index_block with batch 2, GQA 4/2 and heads listed out of order:
