@@ -18,6 +18,7 @@
 #include "select.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace dsa {
 namespace {
@@ -386,18 +387,21 @@ size_t vs_workspace_floats(int n_rows, int Nk) {
 }
 
 // Workgroups of pass 2 that run at once on the current device.
+// Per device, queried once (a racing second query stores the same value).
 static int vs_slots() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, vs_group_pass2_kernel, GT, 0) != hipSuccess || per <= 0)
       per = 1;
-    cached[dev] = cus * per;
+    n = cus * per;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // The chunk size (a multiple of 32 keys in [kVsChunkMin, kVsChunkMax]) that
