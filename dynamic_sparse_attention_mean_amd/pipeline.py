@@ -12,7 +12,12 @@ here it is an input, a list with one entry per Q head carrying the fields
   block, mode, topk, log_alpha, force_first, force_diag   (block rule)
 
 All buffers (index sets, workspaces, outputs) are allocated once in the
-constructor, so a call only enqueues library kernels on the current stream.
+constructor, so a call only enqueues library kernels.  When a layer has both
+Vertical-Slash and block heads, the block index is built on a second stream
+(default priority, with its own workspace) beside the Vertical-Slash index on
+the current stream: the two builders read the same Q and K and write disjoint
+index sets, and neither fills the chip on its own.  The current stream waits
+for both before the attention.
 """
 from __future__ import annotations
 
@@ -77,20 +82,42 @@ class SparsePrefillLayer:
         for (blk, _, _), hs in self.pooled.items():
             ws = max(ws, workspace_size(OP_VS_POOLED, shape, [len(hs), blk]))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
+        # the block builder's own stream and workspace (see the module docstring)
+        self.side = None
+        if self.blk and (self.vs or self.pooled) and torch.device(device).type == "cuda":
+            ws_blk = max(workspace_size(OP_BLOCK, shape, [len(hs), key[0]]) for key, hs in self.blk.items())
+            self.ws_blk = torch.empty(ws_blk, dtype=torch.uint8, device=device)
+            self.side = torch.cuda.Stream(device=device)
+            self.ev_fork = torch.cuda.Event()
+            self.ev_join = torch.cuda.Event()
         odt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
         self.o = torch.empty(B, H, N, 128, dtype=odt, device=device)
         self.lse = torch.empty(B, H, N, dtype=torch.float32, device=device) if want_lse else None
 
+    def _build_block(self, q, k, ws):
+        for (block, mode, topk, la, ff, fd), hs in self.blk.items():
+            build_index_block(q, k, hs, block, mode, topk, self.blk_index, log_alpha=la, force_first=ff,
+                              force_diag=fd, ws=ws)
+
     def build_indices(self, q, k):
+        main = None
+        if self.side is not None:
+            main = torch.cuda.current_stream(q.device)
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            with torch.cuda.stream(self.side):
+                self._build_block(q, k, self.ws_blk)
+            self.ev_join.record(self.side)
         for (sink, local), hs in self.ashape.items():
             build_index_ashape(q, k, hs, sink, local, self.vs_index)
         for (lq, nv, ns), hs in self.vs.items():
             build_index_vs(q, k, hs, lq, nv, ns, self.vs_index, ws=self.ws)
         for (blk, nvb, nsb), hs in self.pooled.items():
             build_index_vs_pooled(q, k, hs, blk, nvb, nsb, self.vs_index, ws=self.ws)
-        for (block, mode, topk, la, ff, fd), hs in self.blk.items():
-            build_index_block(q, k, hs, block, mode, topk, self.blk_index, log_alpha=la, force_first=ff,
-                              force_diag=fd, ws=self.ws)
+        if main is not None:
+            main.wait_event(self.ev_join)
+        else:
+            self._build_block(q, k, self.ws)
 
     def attention(self, q, k, v):
         return sparse_prefill_attn(q, k, v, self.kinds, vs=self.vs_index, blk=self.blk_index,
