@@ -374,7 +374,10 @@ constexpr int OFF_UMASK = 2 * SLOT;
 constexpr int OFF_ULIST = OFF_UMASK + kSmallUnits * 2;
 static_assert(OFF_ULIST + kSmallUnits * 4 <= OFF_MISC, "small-block regions overlap the shared counters");
 
-__device__ __forceinline__ int mod5(int u) { return ((u % NSLOT) + NSLOT) % NSLOT; }
+// Ring slot arithmetic on small non-negative values (unsigned: a multiply-high
+// and a shift, not the signed remainder's fix-ups).
+__device__ __forceinline__ int umod5(int x) { return (int)((uint32_t)x % (uint32_t)NSLOT); }
+__device__ __forceinline__ int addmod5(int a, int b) { const int t = a + b; return t >= NSLOT ? t - NSLOT : t; }
 
 template <bool SMALL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_SIMD))) void attn_kernel(
@@ -642,15 +645,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         // block w - e.  e runs down D (keys ascend), so consecutive e bring in
         // one new block, which is loaded one step ahead into the free slot; the
         // blocks of a step after a gap in D that could not go ahead are loaded at
-        // its start.
+        // its start.  The loop keeps sb = (-ec) mod 5, the slot of block -ec, so
+        // that every slot is sb plus a small non-negative offset, mod 5.
         const uint32_t* sbits = a.sbits + (size_t)it.bh * a.sw;
         const uint32_t* vbits = a.vbits + (size_t)it.bh * a.vw;
         const int32_t* dl = a.dlist + (size_t)it.bh * a.dcap;
         const int emax = min(3 + (it.P0 + 31) / 32, a.dcap - 1);   // wave 3's block still has a key >= 0
         int k = ldc(a.dle, (size_t)it.bh * a.dcap + emax) - 1;
-        auto issue_block = [&](int u) {
+        auto issue_block = [&](int u, int slot) {
           const int k0 = it.P0 + 32 * u;
-          const uint32_t lb = ring + (uint32_t)(mod5(u) * SLOT);
+          const uint32_t lb = ring + (uint32_t)(slot * SLOT);
           if (k0 >= 0 && k0 + 32 <= a.Nk) {
             const char* kb = (const char*)(kbp + (size_t)k0 * 128);
             const char* vb = (const char*)(vbp + (size_t)k0 * 128);
@@ -679,16 +683,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             StepWords sw = {0u, 0u, 0u, 0u};
             const int k0 = it.P0 + 32 * (w - e);
             if (e >= 0 && wave_on && k0 + 31 >= 0) {
+              // two adjacent words each (one load apiece; the column bitmap
+              // has a pad word past its last one)
+              const int c = max(k0, 0) >> 5;
               sw.d0 = ldc(sbits, e + 1);
               sw.d1 = ldc(sbits, e + 2);
-              sw.c0 = ldc(vbits, max(k0, 0) >> 5);
-              sw.c1 = k0 >= 0 ? ldc(vbits, (k0 >> 5) + 1) : 0u;
+              sw.c0 = ldc(vbits, c);
+              sw.c1 = ldc(vbits, c + 1);
+              if (k0 < 0) sw.c1 = 0u;
             }
             return sw;
           };
           int ec = ldc(dl, k);
           int en = k >= 1 ? ldc(dl, k - 1) : -1;
-          for (int u = -ec; u <= 3 - ec; ++u) issue_block(u);
+          int sb = umod5(NSLOT - umod5(ec));       // (-ec) mod 5
+          for (int i = 0; i <= 3; ++i) issue_block(i - ec, addmod5(sb, i));
           take_q();
           StepWords wc = load_words(ec);
           int ep = -1;
@@ -698,18 +707,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             const bool active = wave_on && k0 + 31 >= 0;
             wait_vm();
             __syncthreads();                     // this step's blocks landed; the previous step is done
-            if (ep >= 0) {
+            if (ep > ec + 1) {
+              // after a gap: blocks v = 4 - ep + j (j >= 0) went ahead only
+              // where j mod 5 == 0
               bool late = false;
               for (int v = max(-ec, 4 - ep); v <= 3 - ec; ++v)
-                if (mod5(v - (4 - ep)) != 0) { issue_block(v); late = true; }
+                if (umod5(v - (4 - ep)) != 0) { issue_block(v, umod5(sb + v + ec)); late = true; }
               if (late) {
                 wait_vm();
                 __syncthreads();
               }
             }
-            if (en >= 0) {
+            if (en >= 0 && en == ec - 1) {
+              issue_block(4 - ec, addmod5(sb, 4));   // the one new block of a run
+            } else if (en >= 0) {
               for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
-                if (mod5(v - (4 - ec)) == 0) issue_block(v);
+                if (umod5(v - (4 - ec)) == 0) issue_block(v, umod5(sb + v + ec));
             }
             if (active) {
               // lane row r sees offsets 32 ec + r - c for keys c = 0..31
@@ -721,7 +734,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
                 M = (M | (wc.c0 << (-k0))) & (~0u << (-k0));
               }
               if (ec == 0) M &= causal_mask32(qn);
-              const int sl = mod5(u);
+              const int sl = addmod5(sb, w);
               sub32(sl * SLOT, sl * SLOT + 8192, M);
             }
             // The next step's words and the list entry after it, issued once
@@ -732,6 +745,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             const StepWords wn = load_words(en);
             const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
             if (--k < 0) break;
+            sb = en == ec - 1 ? addmod5(sb, 1) : umod5(sb + ec - en);   // (-en) mod 5
             ep = ec;
             ec = en;
             en = enn;
