@@ -577,14 +577,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
 
       // One 32x32 sub-block: S^T over the 32 keys at kofs, the online softmax
       // under the mask M, O^T += V^T P^T with the V rows at vofs.
-      auto sub32 = [&](uint32_t kofs, uint32_t vofs, uint32_t M) {
+      // `sparse`: the mask is rarely full (Vertical-Slash), so it is applied
+      // without first testing for a full mask.
+      auto sub32 = [&](uint32_t kofs, uint32_t vofs, uint32_t M, bool sparse = false) {
         if (!row_ok) M = 0u;
-        if (__builtin_amdgcn_ballot_w64(M != 0u) == 0) return;
+        const uint64_t blo = __builtin_amdgcn_ballot_w64((M & 0xFFFFu) != 0u);
+        const uint64_t bhi = __builtin_amdgcn_ballot_w64((M >> 16) != 0u);
+        if ((blo | bhi) == 0) return;
         f32x16 sacc;
         qk32(kofs, sacc);
-        if (__builtin_amdgcn_ballot_w64(M != ~0u) != 0) mask32(sacc, M);
-        const uint32_t halves = (__builtin_amdgcn_ballot_w64((M & 0xFFFFu) != 0u) != 0 ? 1u : 0u) |
-                                (__builtin_amdgcn_ballot_w64((M >> 16) != 0u) != 0 ? 2u : 0u);
+        if (sparse || __builtin_amdgcn_ballot_w64(M != ~0u) != 0) mask32(sacc, M);
+        const uint32_t halves = (blo != 0 ? 1u : 0u) | (bhi != 0 ? 2u : 0u);
         const float muse = grow_to(lane_max(sacc));
         pv32(sacc, muse, vofs, halves);
       };
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               }
               if (ec == 0) M &= causal_mask32(qn);
               const int sl = addmod5(sb, w);
-              sub32(sl * SLOT, sl * SLOT + 8192, M);
+              sub32(sl * SLOT, sl * SLOT + 8192, M, true);
             }
             // The next step's words and the list entry after it, issued once
             // this step's LDS reads are done: scalar loads and LDS reads share
