@@ -687,13 +687,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             const int k0 = it.P0 + 32 * (w - e);
             if (e >= 0 && wave_on && k0 + 31 >= 0) {
               // two adjacent words each (one load apiece; the column bitmap
-              // has a pad word past its last one)
+              // has a pad word past its last one).  c1 is used only when
+              // k0 >= 0; nothing here reads a loaded word, so no wait for the
+              // loads falls inside this step.
               const int c = max(k0, 0) >> 5;
               sw.d0 = ldc(sbits, e + 1);
               sw.d1 = ldc(sbits, e + 2);
               sw.c0 = ldc(vbits, c);
               sw.c1 = ldc(vbits, c + 1);
-              if (k0 < 0) sw.c1 = 0u;
             }
             return sw;
           };
