@@ -647,9 +647,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         // P0 + 32 u in ring slot u mod 5; the step for offset e gives wave w the
         // block w - e.  e runs down D (keys ascend), so consecutive e bring in
         // one new block, which is loaded one step ahead into the free slot; the
-        // blocks of a step after a gap in D that could not go ahead are loaded at
-        // its start.  The loop keeps sb = (-ec) mod 5, the slot of block -ec, so
-        // that every slot is sb plus a small non-negative offset, mod 5.
+        // blocks of a step after a gap in D that could not go ahead are loaded
+        // in the step before it, once every wave has read that step's slots.
+        // The loop keeps sb = (-ec) mod 5, the slot of block -ec, so that every
+        // slot is sb plus a small non-negative offset, mod 5.
         const uint32_t* sbits = a.sbits + (size_t)it.bh * a.sw;
         const uint32_t* vbits = a.vbits + (size_t)it.bh * a.vw;
         const int32_t* dl = a.dlist + (size_t)it.bh * a.dcap;
@@ -704,24 +705,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           for (int i = 0; i <= 3; ++i) issue_block(i - ec, addmod5(sb, i));
           take_q();
           StepWords wc = load_words(ec);
-          int ep = -1;
           while (true) {
             const int u = w - ec;
             const int k0 = it.P0 + 32 * u;
             const bool active = wave_on && k0 + 31 >= 0;
             wait_vm();
             __syncthreads();                     // this step's blocks landed; the previous step is done
-            if (ep > ec + 1) {
-              // after a gap: blocks v = 4 - ep + j (j >= 0) went ahead only
-              // where j mod 5 == 0
-              bool late = false;
-              for (int v = max(-ec, 4 - ep); v <= 3 - ec; ++v)
-                if (umod5(v - (4 - ep)) != 0) { issue_block(v, umod5(sb + v + ec)); late = true; }
-              if (late) {
-                wait_vm();
-                __syncthreads();
-              }
-            }
             if (en >= 0 && en == ec - 1) {
               issue_block(4 - ec, addmod5(sb, 4));   // the one new block of a run
             } else if (en >= 0) {
@@ -741,6 +730,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
               const int sl = addmod5(sb, w);
               sub32(sl * SLOT, sl * SLOT + 8192, M, true);
             }
+            if (en >= 0 && ec - en >= 2) {
+              // Before a gap in D: the next step's blocks that could not go into
+              // the free slot are loaded here, once every wave is done with this
+              // step's slots, rather than at the next step's start.
+              __syncthreads();
+              for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
+                if (umod5(v - (4 - ec)) != 0) issue_block(v, umod5(sb + v + ec));
+            }
             // The next step's words and the list entry after it, issued once
             // this step's LDS reads are done: scalar loads and LDS reads share
             // one counter, so issued earlier, the step's first LDS wait would
@@ -750,7 +747,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
             if (--k < 0) break;
             sb = en == ec - 1 ? addmod5(sb, 1) : umod5(sb + ec - en);   // (-en) mod 5
-            ep = ec;
             ec = en;
             en = enn;
             wc = wn;
