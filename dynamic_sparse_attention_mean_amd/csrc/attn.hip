@@ -86,7 +86,6 @@ __device__ __forceinline__ int arg_i8(const int8_t* t, int i) {
 }
 
 // ------------------------------------------------------------------ bitmaps
-__device__ __forceinline__ bool test_bit(const uint32_t* bm, int i) { return (bm[i >> 5] >> (i & 31)) & 1u; }
 
 // any bit set in [lo, hi] (inclusive, 0 <= lo <= hi) of an unpadded bitmap
 __device__ bool range_any(const uint32_t* bm, int lo, int hi) {
@@ -121,17 +120,61 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
   }
 }
 
-// Sub-block offsets e in [0, ND): e is in D iff the offsets [32e - 31, 32e + 31]
-// hold a selected diagonal.  D is written as a bitmap, as an ascending list and
-// as the prefix counts #{e' in D : e' <= e}.  A head whose lists are exactly
-// cols = [0, S) and diags = [0, L) (the A-shape sets: sink S, local window L)
-// is marked as a window head: its mask is closed-form and runs on whole tiles.
-__global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, int ND) {
+// Step centres of a Vertical-Slash head.  A 32x32 sub-block whose rows start at
+// position R and whose keys start at R - c holds the offsets i - j in
+// [c - 31, c + 31], offset c on all 32 rows.  A set C of such centres, any two
+// at least 32 apart, visits every (i, j) at most once in each wave's key
+// blocks; it visits every row of offset o iff o is a centre or lies between
+// two centres exactly 32 apart.  C is built greedily over the selected offsets
+// in ascending order: an offset already covered is skipped, one within 32 of
+// the last centre extends the run by a centre 32 further on, and any other
+// offset starts a new run centred on itself.  So a band of W consecutive
+// offsets costs 1 + ceil((W - 1) / 32) sub-blocks per wave, and a lone diagonal
+// one.  An offset with no selected offset in the 63 before it always starts a
+// run; each thread takes the run starts of one bitmap word and follows the
+// greedy from there until the next such offset.
+//
+// Outputs per head: the centres ascending, each with the 64 diagonal bits of
+// offsets [c - 32, c + 31] ({c, bits 0-31, bits 32-63, 0}); a bitmap of the
+// centres; and the prefix counts #{c in C : c <= 32 x + 31}.  A head whose lists
+// are exactly cols = [0, S) and diags = [0, L) (the A-shape sets: sink S, local
+// window L) is marked as a window head: its mask is closed-form and runs on
+// whole tiles.
+__device__ __forceinline__ int next_set_within(const uint32_t* bm, int nwords, int lo, int hi) {
+  // first set bit in [lo, hi] of an unpadded bitmap of nwords words, or -1
+  for (int wd = lo >> 5; wd <= (hi >> 5) && wd < nwords; ++wd) {
+    uint32_t m = bm[wd];
+    if (wd == (lo >> 5)) m &= ~0u << (lo & 31);
+    if (m) {
+      const int o = 32 * wd + __builtin_ctz(m);
+      return o <= hi ? o : -1;
+    }
+  }
+  return -1;
+}
+
+// The greedy of one run start s: calls f(c) for each centre, in order, until
+// the next offset that starts a run of its own.
+template <typename F>
+__device__ void follow_run(const uint32_t* sb, int nwords, int s, F&& f) {
+  int c = s;
+  f(c);
+  while (true) {
+    // the next selected offset after c; one more than 63 past c starts a run
+    const int o = next_set_within(sb, nwords, c + 1, c + 63);
+    if (o < 0 || !range_any(sb, max(0, o - 63), o - 1)) break;
+    c = o <= c + 32 ? c + 32 : o;
+    f(c);
+  }
+}
+
+__global__ __launch_bounds__(256) void vs_centres_kernel(AttnArgs a, BhList L, int ND) {
   const int bh = L.bh[blockIdx.x];
-  const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view
-  uint32_t* db = a.dbits + (size_t)bh * a.dw;
-  int32_t* dl = a.dlist + (size_t)bh * a.dcap;
-  int32_t* dle = a.dle + (size_t)bh * a.dcap;
+  const uint32_t* sp = a.sbits + (size_t)bh * a.sw;         // padded: two zero words first
+  const uint32_t* sb = sp + 2;                              // unpadded view
+  uint32_t* cb = a.cbits + (size_t)bh * a.cw;
+  int32_t* cl = a.clist + (size_t)bh * a.ccap * 4;
+  int32_t* cle = a.cle + (size_t)bh * a.ccap;
   __shared__ int s_wave[4];
   __shared__ int s_base;
   __shared__ int s_prefix;
@@ -155,27 +198,68 @@ __global__ __launch_bounds__(256) void vs_dsteps_kernel(AttnArgs a, BhList L, in
     }
   }
   const int w = threadIdx.x >> 6;
-  for (int e0 = 0; e0 < ND; e0 += 256) {
-    const int e = e0 + threadIdx.x;
-    bool in = false;
-    if (e < ND) {
-      const int lo = max(0, 32 * e - 31), hi = min(a.Nk - 1, 32 * e + 31);
-      in = lo <= hi && range_any(sb, lo, hi);
-      if (in) atomicOr(&db[e >> 5], 1u << (e & 31));
+  const int nwords = (a.Nk + 31) / 32;
+  for (int x0 = 0; x0 < nwords; x0 += 256) {
+    const int x = x0 + threadIdx.x;
+    // the run start in word x, if any (two run starts are more than 63 apart)
+    int start = -1;
+    if (x < nwords) {
+      uint32_t m = sb[x];
+      if (m) {
+        int last = -1000;
+        for (int y = max(0, x - 2); y < x; ++y)
+          if (sb[y]) last = 32 * y + 31 - __builtin_clz(sb[y]);
+        while (m) {
+          const int o = 32 * x + __builtin_ctz(m);
+          if (o - last > 63) { start = o; break; }
+          last = o;
+          m &= m - 1;
+        }
+      }
     }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(in);
-    const uint32_t rank = ballot_rank(bal);
-    if ((threadIdx.x & 63) == 0) s_wave[w] = __popcll(bal);
+    int cnt = 0;
+    if (start >= 0) follow_run(sb, nwords, start, [&](int) { ++cnt; });
+    // exclusive prefix of the counts over the workgroup
+    const uint32_t incl = wave_incl_scan((uint32_t)cnt);
+    if ((threadIdx.x & 63) == 63) s_wave[w] = (int)incl;
     __syncthreads();
-    int off = s_base;
+    int off = s_base + (int)incl - cnt;
     for (int i = 0; i < w; ++i) off += s_wave[i];
-    if (in) dl[off + rank] = e;
-    if (e < ND) dle[e] = off + rank + (in ? 1 : 0);
+    if (start >= 0) {
+      follow_run(sb, nwords, start, [&](int c) {
+        const int i = (c >> 5) + 1, s = c & 31;               // padded word holding offset c - 32
+        const uint64_t lo = ((uint64_t)sp[i + 1] << 32) | sp[i];
+        const uint64_t win = s == 0 ? lo : (lo >> s) | ((uint64_t)sp[i + 2] << (64 - s));
+        int32_t* e = cl + 4 * (size_t)off;
+        e[0] = c;
+        e[1] = (int32_t)(uint32_t)win;
+        e[2] = (int32_t)(uint32_t)(win >> 32);
+        e[3] = 0;
+        cb[c >> 5] = 1u << (c & 31);                            // one centre per word at most
+        ++off;
+      });
+    }
     __syncthreads();
     if (threadIdx.x == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.dcount[bh] = s_base;
+  // prefix counts per 32 positions (the bitmap holds at most one centre per word)
+  if (threadIdx.x == 0) s_prefix = 0;
+  __syncthreads();
+  for (int x0 = 0; x0 < ND; x0 += 256) {
+    const int x = x0 + threadIdx.x;
+    const bool in = x < ND && cb[x] != 0u;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(in);
+    if ((threadIdx.x & 63) == 0) s_wave[w] = __popcll(bal);
+    __syncthreads();
+    int off = s_prefix;
+    for (int i = 0; i < w; ++i) off += s_wave[i];
+    if (x < ND) cle[x] = off + (int)ballot_rank(bal) + (in ? 1 : 0);
+    __syncthreads();
+    if (threadIdx.x == 0) s_prefix += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.ccount[bh] = s_base;
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -216,6 +300,9 @@ typedef const __attribute__((address_space(4))) int32_t c_i32_t;
 typedef const __attribute__((address_space(4))) uint32_t c_u32_t;
 __device__ __forceinline__ int ldc(const int32_t* p, size_t i) { return ((c_i32_t*)p)[i]; }
 __device__ __forceinline__ uint32_t ldc(const uint32_t* p, size_t i) { return ((c_u32_t*)p)[i]; }
+typedef const __attribute__((address_space(4))) u32x4 c_u32x4_t;
+// entry i of an array of 16-byte records, as one scalar load
+__device__ __forceinline__ u32x4 ldc4(const int32_t* p, size_t i) { return ((c_u32x4_t*)p)[i]; }
 
 // One entry of a pair's tile stream.
 struct Entry {
@@ -614,7 +701,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       };
 
       int gcursor = 0, gcount = 0;
-      const uint32_t* dbits = nullptr;
+      const uint32_t* cbits = nullptr;
       if (it.kind == 1 && ldc(a.win, 2 * (size_t)it.bh) >= 0) {
         // window head: key tiles of the sink [0, S) and of the window
         // [P0 - L + 1, last_pos], merged when they meet
@@ -638,26 +725,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           it.nent = ts + (tend - tw0);
         }
       } else if (it.kind == 1) {
-        dbits = a.dbits + (size_t)it.bh * a.dw;
+        cbits = a.cbits + (size_t)it.bh * a.cw;
         gcount = min(ldc(a.cols_count, it.bh), a.cols_cap);
         // the arena is reused below: every wave has read the item number
         __syncthreads();
 
-        // ---- Vertical-Slash sub-block steps.  Block u holds the 32 keys from
-        // P0 + 32 u in ring slot u mod 5; the step for offset e gives wave w the
-        // block w - e.  e runs down D (keys ascend), so consecutive e bring in
-        // one new block, which is loaded one step ahead into the free slot; the
-        // blocks of a step after a gap in D that could not go ahead are loaded
-        // in the step before it, once every wave has read that step's slots.
-        // The loop keeps sb = (-ec) mod 5, the slot of block -ec, so that every
-        // slot is sb plus a small non-negative offset, mod 5.
-        const uint32_t* sbits = a.sbits + (size_t)it.bh * a.sw;
+        // ---- Vertical-Slash sub-block steps over the head's step centres c,
+        // descending (keys ascend): the step of centre c gives wave w the 32 keys
+        // from P0 + 32 w - c, in ring slot sb + w (mod 5).  Within a run (the next
+        // centre is c - 32) wave w next takes the block wave w + 1 used, so a step
+        // brings in one new block, loaded one step ahead into the free slot
+        // sb + 4.  The first step of a new run needs four new blocks: wave 0's
+        // goes into the free slot during the step before, the other three into
+        // the slots that step used, once every wave is done with them.
         const uint32_t* vbits = a.vbits + (size_t)it.bh * a.vw;
-        const int32_t* dl = a.dlist + (size_t)it.bh * a.dcap;
-        const int emax = min(3 + (it.P0 + 31) / 32, a.dcap - 1);   // wave 3's block still has a key >= 0
-        int k = ldc(a.dle, (size_t)it.bh * a.dcap + emax) - 1;
-        auto issue_block = [&](int u, int slot) {
-          const int k0 = it.P0 + 32 * u;
+        const int32_t* cl = a.clist + (size_t)it.bh * a.ccap * 4;
+        const int cmax = it.P0 + 127;            // wave 3's block still has a key >= 0
+        int k = ldc(a.cle, (size_t)it.bh * a.ccap + min(cmax >> 5, a.ccap - 1)) - 1;
+        if (k >= 0 && ldc(cl, 4 * (size_t)k) > cmax) --k;   // one centre at most per 32 positions
+        auto issue_keys = [&](int k0, int slot) {
           const uint32_t lb = ring + (uint32_t)(slot * SLOT);
           if (k0 >= 0 && k0 + 32 <= a.Nk) {
             const char* kb = (const char*)(kbp + (size_t)k0 * 128);
@@ -676,77 +762,70 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         };
         if (k >= 0) {
           const bool wave_on = R0w <= it.last_pos;
-          // Scalar words a step needs: the diagonal bitmap words of its offset
-          // window and this wave's column words.  They are loaded one step
-          // ahead, with the list entry two steps ahead, so that their latency
-          // hides behind a step's arithmetic.
-          struct StepWords {
-            uint32_t d0, d1, c0, c1;
+          // A step's entry {c, diagonal bits of offsets [c - 32, c + 31]} is
+          // loaded two steps ahead and this wave's column words one step ahead
+          // (scalar loads), so that their latency hides behind a step.
+          struct ColWords {
+            uint32_t c0, c1;
           };
-          auto load_words = [&](int e) {
-            StepWords sw = {0u, 0u, 0u, 0u};
-            const int k0 = it.P0 + 32 * (w - e);
-            if (e >= 0 && wave_on && k0 + 31 >= 0) {
-              // two adjacent words each (one load apiece; the column bitmap
-              // has a pad word past its last one).  c1 is used only when
-              // k0 >= 0; nothing here reads a loaded word, so no wait for the
-              // loads falls inside this step.
-              const int c = max(k0, 0) >> 5;
-              sw.d0 = ldc(sbits, e + 1);
-              sw.d1 = ldc(sbits, e + 2);
-              sw.c0 = ldc(vbits, c);
-              sw.c1 = ldc(vbits, c + 1);
+          auto load_cols = [&](int c) {
+            ColWords x = {0u, 0u};
+            const int k0 = it.P0 + 32 * w - c;
+            if (c >= 0 && wave_on && k0 + 31 >= 0) {
+              // two adjacent words (the bitmap has a pad word past its last
+              // one); c1 is used only when k0 >= 0
+              const int cw = max(k0, 0) >> 5;
+              x.c0 = ldc(vbits, cw);
+              x.c1 = ldc(vbits, cw + 1);
             }
-            return sw;
+            return x;
           };
-          int ec = ldc(dl, k);
-          int en = k >= 1 ? ldc(dl, k - 1) : -1;
-          int sb = umod5(NSLOT - umod5(ec));       // (-ec) mod 5
-          for (int i = 0; i <= 3; ++i) issue_block(i - ec, addmod5(sb, i));
+          const u32x4 none = {~0u, 0u, 0u, 0u};
+          u32x4 ec = ldc4(cl, k);
+          u32x4 en = k >= 1 ? ldc4(cl, k - 1) : none;
+          int sb = 0;
+          for (int i = 0; i <= 3; ++i) issue_keys(it.P0 + 32 * i - (int)ec[0], i);
           take_q();
-          StepWords wc = load_words(ec);
+          ColWords wc = load_cols((int)ec[0]);
           while (true) {
-            const int u = w - ec;
-            const int k0 = it.P0 + 32 * u;
+            const int cc = (int)ec[0], cn = (int)en[0];
+            const int k0 = it.P0 + 32 * w - cc;
             const bool active = wave_on && k0 + 31 >= 0;
+            const bool run = cn >= 0 && cn == cc - 32;
             wait_vm();
             __syncthreads();                     // this step's blocks landed; the previous step is done
-            if (en >= 0 && en == ec - 1) {
-              issue_block(4 - ec, addmod5(sb, 4));   // the one new block of a run
-            } else if (en >= 0) {
-              for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
-                if (umod5(v - (4 - ec)) == 0) issue_block(v, umod5(sb + v + ec));
-            }
+            if (run) issue_keys(it.P0 + 128 - cc, addmod5(sb, 4));      // the one new block of a run
+            else if (cn >= 0) issue_keys(it.P0 - cn, addmod5(sb, 4));   // wave 0's block of the next run
             if (active) {
-              // lane row r sees offsets 32 ec + r - c for keys c = 0..31
-              const uint64_t dwin = ((uint64_t)wc.d1 << 32) | wc.d0;
+              // lane row r sees offsets cc + r - j for keys j = 0..31: bits
+              // 32 + r - j of the entry's window
+              const uint64_t dwin = ((uint64_t)ec[2] << 32) | ec[1];
               uint32_t M = __builtin_bitreverse32((uint32_t)(dwin >> (1 + qn)));
               if (k0 >= 0) {
                 M |= (uint32_t)((((uint64_t)wc.c1 << 32) | wc.c0) >> (k0 & 31));
               } else {
                 M = (M | (wc.c0 << (-k0))) & (~0u << (-k0));
               }
-              if (ec == 0) M &= causal_mask32(qn);
+              if (cc < 31) M &= causal_mask32(qn + cc);
               const int sl = addmod5(sb, w);
               sub32(sl * SLOT, sl * SLOT + 8192, M, true);
             }
-            if (en >= 0 && ec - en >= 2) {
-              // Before a gap in D: the next step's blocks that could not go into
-              // the free slot are loaded here, once every wave is done with this
-              // step's slots, rather than at the next step's start.
+            if (cn >= 0 && !run) {
+              // Before a new run: its other three blocks go into the slots of
+              // this step, once every wave is done with them.
               __syncthreads();
-              for (int v = max(-en, 4 - ec); v <= 3 - en; ++v)
-                if (umod5(v - (4 - ec)) != 0) issue_block(v, umod5(sb + v + ec));
+#pragma unroll
+              for (int v = 1; v <= 3; ++v) issue_keys(it.P0 + 32 * v - cn, umod5(sb + 4 + v));
             }
-            // The next step's words and the list entry after it, issued once
-            // this step's LDS reads are done: scalar loads and LDS reads share
-            // one counter, so issued earlier, the step's first LDS wait would
-            // also wait for them.  Here their latency overlaps the next step's
-            // DMA wait and barrier.
-            const StepWords wn = load_words(en);
-            const int enn = k >= 2 ? ldc(dl, k - 2) : -1;
+            // The next step's words and the entry after it, issued once this
+            // step's LDS reads are done: scalar loads and LDS reads share one
+            // counter, so issued earlier, the step's first LDS wait would also
+            // wait for them.  Here their latency overlaps the next step's DMA
+            // wait and barrier.
+            const ColWords wn = load_cols(cn);
+            const u32x4 enn = k >= 2 ? ldc4(cl, k - 2) : none;
             if (--k < 0) break;
-            sb = en == ec - 1 ? addmod5(sb, 1) : umod5(sb + ec - en);   // (-en) mod 5
+            sb = run ? addmod5(sb, 1) : addmod5(sb, 4);
             ec = en;
             en = enn;
             wc = wn;
@@ -916,12 +995,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
             if (idx < gcount) {
               j = cols[idx];
               if (j >= 0 && j <= it.last_pos) {
-                const int uj = (j - it.P0) >> 5;      // floor division
                 cov = 0u;
 #pragma unroll
                 for (int w4 = 0; w4 < 4; ++w4) {
-                  const int e = w4 - uj;
-                  const bool c = e < 0 || it.P0 + 32 * w4 > it.last_pos || (e < a.dcap && test_bit(dbits, e));
+                  // wave w4's block holds key j at the steps of centres in [lo, lo + 31]
+                  const int lo = it.P0 + 32 * w4 - j;
+                  const bool c = lo + 31 < 0 || it.P0 + 32 * w4 > it.last_pos ||
+                                 range_any(cbits, max(lo, 0), min(lo + 31, 32 * a.cw - 1));
                   cov |= (c ? 1u : 0u) << w4;
                 }
                 keep = cov != 0xFu;
@@ -1088,26 +1168,27 @@ int cu_count() {
 }
 
 struct VsLayout {
-  int sw, vw, dw, ND;
-  size_t off_s, off_v, off_d, off_dc, off_ctr, off_dl, off_dle, off_win, total_words;
+  int sw, vw, cw, ND;
+  size_t off_s, off_v, off_c, off_cc, off_ctr, off_cl, off_cle, off_win, total_words;
 };
 
 VsLayout vs_layout(int B, int H, int Nk) {
   VsLayout L;
   L.sw = (Nk + 31) / 32 + 5;
   L.vw = (Nk + 31) / 32 + 2;
-  L.ND = (Nk + 30) / 32 + 1;     // e with 32e - 31 <= Nk - 1
-  L.dw = (L.ND + 31) / 32 + 1;
+  L.ND = (Nk + 30) / 32 + 1;     // centres lie in [0, Nk + 30]: at most one per 32 positions
+  L.cw = L.ND;
   const size_t nbh = (size_t)B * H;
   size_t off = 0;
   L.off_ctr = off; off += 64;
   L.off_s = off; off += nbh * L.sw;
   L.off_v = off; off += nbh * L.vw;
-  L.off_d = off; off += nbh * L.dw;
-  L.off_dc = off; off += nbh;
+  L.off_c = off; off += nbh * L.cw;
+  L.off_cc = off; off += nbh;
   L.total_words = off;          // region zeroed before every call
-  L.off_dl = off; off += nbh * L.ND;
-  L.off_dle = off; off += nbh * L.ND;
+  off = (off + 3) & ~size_t(3);  // 16-byte entries, read as one scalar load each
+  L.off_cl = off; off += nbh * L.ND * 4;
+  L.off_cle = off; off += nbh * L.ND;
   L.off_win = off; off += nbh * 2;
   (void)off;
   return L;
@@ -1162,12 +1243,12 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   a.counters = (int32_t*)(base + L.off_ctr);
   a.sbits = base + L.off_s;
   a.vbits = base + L.off_v;
-  a.dbits = base + L.off_d;
-  a.dcount = (int32_t*)(base + L.off_dc);
-  a.dlist = (int32_t*)(base + L.off_dl);
-  a.dle = (int32_t*)(base + L.off_dle);
+  a.cbits = base + L.off_c;
+  a.ccount = (int32_t*)(base + L.off_cc);
+  a.clist = (int32_t*)(base + L.off_cl);
+  a.cle = (int32_t*)(base + L.off_cle);
   a.win = (int32_t*)(base + L.off_win);
-  a.sw = L.sw; a.vw = L.vw; a.dw = L.dw; a.dcap = L.ND;
+  a.sw = L.sw; a.vw = L.vw; a.cw = L.cw; a.ccap = L.ND;
 
   hipError_t e = launch_zero_u32(base, L.total_words, st);
   if (e != hipSuccess) return e;
@@ -1180,7 +1261,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
       if (a.kind[h] == 1) vs.bh[vs.n++] = (int16_t)(b * a.H + h);
   if (vs.n > 0) {
     hipLaunchKernelGGL(vs_setbits_kernel, dim3(8, vs.n), dim3(256), 0, st, a, vs);
-    hipLaunchKernelGGL(vs_dsteps_kernel, dim3(vs.n), dim3(256), 0, st, a, vs, L.ND);
+    hipLaunchKernelGGL(vs_centres_kernel, dim3(vs.n), dim3(256), 0, st, a, vs, L.ND);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 

@@ -110,9 +110,10 @@ struct AttnArgs {
   const int32_t* cols; const int32_t* cols_count; int cols_cap;
   const int32_t* diags; const int32_t* diags_count; int diags_cap;
   uint32_t* sbits; uint32_t* vbits;  // diagonal bitmap (two leading pad words), column bitmap
-  uint32_t* dbits;                   // bit e set iff a selected diagonal lies in [32e - 31, 32e + 31]
-  int32_t* dlist; int32_t* dcount; int32_t* dle;   // those e ascending, their number, #{e' <= e}
-  int sw, vw, dw, dcap;              // words per head of each bitmap; dlist capacity
+  uint32_t* cbits;                   // bit c set iff c is a step centre (offsets of the sub-block steps)
+  int32_t* clist;                    // the centres ascending: {c, diagonal bits of [c - 32, c + 31] (2 words), 0}
+  int32_t* ccount; int32_t* cle;     // their number; #{centres <= 32 x + 31} for x in [0, ccap)
+  int sw, vw, cw, ccap;              // words per head of each bitmap; clist capacity (entries)
   int32_t* win;                      // [B*H][2]: window length and sink of a head whose sets are
                                      // cols = [0, sink), diags = [0, window) (else window = -1)
   // Block sets

@@ -48,14 +48,18 @@ def round_bf16_np(x):
 
 
 def check_outputs(got32, got16, ref_o, ref_l, lse, what):
-    """fp32 path at the acceptance bar; bf16 path per element at max(1e-2, half
-    an ulp) and on average at 1e-3 plus the storage rounding of the exact values."""
+    """fp32 path at the acceptance bar.  The bf16 path (the fp32 output rounded
+    to nearest even, checked bit for bit by run_layer) per element within
+    max(1e-2, half an ulp of the stored value plus the fp32 error), which is
+    what storing an fp32 result within the bar can cost, and on average within
+    1e-3 plus the storage rounding of the exact values."""
     err = np.abs(got32 - ref_o)
     assert np.isfinite(got32).all(), f"{what}: non-finite outputs"
     assert err.max() <= MAX_ABS, f"{what}: fp32 max abs err {err.max():.3g}"
     assert err.mean() <= MEAN_ABS, f"{what}: fp32 mean abs err {err.mean():.3g}"
     e16 = np.abs(got16 - ref_o)
-    assert np.all(e16 <= np.maximum(MAX_ABS, half_ulp_bf16(ref_o))), f"{what}: bf16 max abs err {e16.max():.3g}"
+    bound16 = np.maximum(MAX_ABS, half_ulp_bf16(got32) + err)
+    assert np.all(e16 <= bound16 * (1 + 1e-12)), f"{what}: bf16 max abs err {e16.max():.3g}"
     storage = np.abs(round_bf16_np(ref_o) - ref_o).mean()
     assert e16.mean() <= MEAN_ABS + storage, f"{what}: bf16 mean abs err {e16.mean():.3g} (storage {storage:.3g})"
     fin = np.isfinite(ref_l)

@@ -118,3 +118,45 @@ def test_token_heads_mixed_with_other_kinds():
         else:
             ref_o, ref_l = oracle_attention_rows(w, sets, 0, h, rows)
         assert_attention_close(o[0, h], lse[0, h], ref_o, ref_l, f"mixed-with-tokens h={h}")
+
+
+def _bands(start, widths, gaps, n):
+    """Offsets of bands of the given widths separated by the given gaps."""
+    out, o = [], start
+    for wd, gp in zip(widths, gaps):
+        out.extend(range(o, min(n, o + wd)))
+        o += wd + gp
+    return np.array(sorted(set(x for x in out if x < n)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("Nk,Nq", [(1200, 1200), (1000, 333), (700, 129)])
+def test_vertical_slash_constructed_sets(Nk, Nq):
+    """Vertical-Slash attention on hand-built sets that stress the sub-block
+    step schedule: bands of 1 to 100 consecutive diagonals separated by gaps
+    on both sides of 32 and 63 (where a run may or may not continue), lone
+    diagonals next to offset 0 (sub-blocks that cross the causal edge) and at
+    the last offset, every offset at once, columns only, and both empty.  The
+    oracle is given the same sets."""
+    rng = np.random.default_rng(Nk + Nq)
+    widths = [1, 1, 33, 64, 65, 31, 32, 1, 100, 2, 1, 40]
+    gaps = [32, 33, 62, 63, 64, 65, 96, 97, 128, 31, 1, 0]
+    S0 = _bands(0, widths, gaps, Nk)
+    S1 = _bands(5, widths[::-1], gaps[::-1], Nk)
+    S2 = np.array(sorted({1, 2, 31, 32, 33, 95, Nk - 1} | set(rng.choice(Nk, 40, replace=False).tolist())),
+                  dtype=np.int64)
+    S3 = np.arange(Nk, dtype=np.int64)
+    cols = lambda n: np.sort(rng.choice(Nk, n, replace=False)).astype(np.int64)
+    plan = [(cols(30), S0), (cols(5), S1), (np.array([0, 1, Nk - 1], dtype=np.int64), S2), (cols(12), S3),
+            (cols(50), np.zeros(0, dtype=np.int64)), (np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64))]
+    H = len(plan)
+    heads = [vs(64, 1, 1) for _ in range(H)]
+    w = workload(70 + Nq, 1, H, 2 if H % 2 == 0 else 1, Nk, heads, Nq=Nq)
+    sets = {(0, h): ("vs", V, S, None, None) for h, (V, S) in enumerate(plan)}
+    kinds, vsi, bi = upload_sets(w, sets, DEV)
+    o, lse = dsa.sparse_prefill_attn(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), kinds, vs=vsi, out_dtype=dsa.OUT_F32)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    rows = list(range(Nq))
+    for (b, h) in sets:
+        ref_o, ref_l = oracle_attention_rows(w, sets, b, h, rows)
+        assert_attention_close(o[b, h], lse[b, h], ref_o, ref_l, f"constructed sets h={h}")
