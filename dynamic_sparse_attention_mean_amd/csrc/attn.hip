@@ -140,48 +140,74 @@ __global__ void vs_setbits_kernel(AttnArgs a, BhList L) {
 // are exactly cols = [0, S) and diags = [0, L) (the A-shape sets: sink S, local
 // window L) is marked as a window head: its mask is closed-form and runs on
 // whole tiles.
-__device__ __forceinline__ int next_set_within(const uint32_t* bm, int nwords, int lo, int hi) {
-  // first set bit in [lo, hi] of an unpadded bitmap of nwords words, or -1
-  for (int wd = lo >> 5; wd <= (hi >> 5) && wd < nwords; ++wd) {
-    uint32_t m = bm[wd];
-    if (wd == (lo >> 5)) m &= ~0u << (lo & 31);
-    if (m) {
-      const int o = 32 * wd + __builtin_ctz(m);
-      return o <= hi ? o : -1;
-    }
-  }
-  return -1;
+// Diagonal bitmaps of up to this many words are staged in LDS by the compile
+// step (the greedy's reads are then LDS reads); longer ones are read in place.
+constexpr int kCentreLdsWords = 16384;
+
+// 64 bits of a bitmap window w[0..4] (bit 0 of w[0] at position p0), from
+// bit position lo on (p0 <= lo <= p0 + 95).
+__device__ __forceinline__ uint64_t window64(const uint32_t (&w)[5], int p0, int lo) {
+  const int rel = lo - p0, k = rel >> 5, sh = rel & 31;
+  const uint64_t a = ((uint64_t)w[k + 1] << 32) | w[k];
+  return sh == 0 ? a : (a >> sh) | ((uint64_t)w[k + 2] << (64 - sh));
 }
 
-// The greedy of one run start s: calls f(c) for each centre, in order, until
-// the next offset that starts a run of its own.
-template <typename F>
-__device__ void follow_run(const uint32_t* sb, int nwords, int s, F&& f) {
+// The greedy of one run start s over a head's unpadded diagonal bitmap
+// (word(i): word i, zero outside the bitmap): calls f(c) for each centre, in
+// order, until the next offset that starts a run of its own.  An offset within
+// 32 of the last centre c never does (the last selected offset before it lies
+// in [c - 31, c]); one further on does when none of the 63 offsets before it
+// is selected.  Each step reads the five words around c at once.
+template <typename Word, typename F>
+__device__ void follow_run(const Word& word, int s, F&& f) {
   int c = s;
   f(c);
   while (true) {
-    // the next selected offset after c; one more than 63 past c starts a run
-    const int o = next_set_within(sb, nwords, c + 1, c + 63);
-    if (o < 0 || !range_any(sb, max(0, o - 63), o - 1)) break;
-    c = o <= c + 32 ? c + 32 : o;
+    const int b = (c - 62) >> 5;                          // floor division
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = word(b + i);
+    const uint64_t nx = window64(w, 32 * b, c + 1) & (~0ull >> 1);   // offsets c + 1 .. c + 63
+    if (nx == 0) break;
+    const int o = c + 1 + __builtin_ctzll(nx);
+    if (o <= c + 32) {
+      c += 32;
+    } else {
+      if ((window64(w, 32 * b, o - 63) & (~0ull >> 1)) == 0) break;   // offsets o - 63 .. o - 1
+      c = o;
+    }
     f(c);
   }
 }
 
+// Workgroup barrier for LDS data only: unlike __syncthreads it does not wait
+// for this wave's global stores (the compile step's outputs) to complete.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Exclusive prefix sum of v over a 256-thread workgroup (s: 4 ints of LDS).
+__device__ __forceinline__ int block_excl_scan(int v, int* s) {
+  const int w = threadIdx.x >> 6;
+  const int incl = (int)wave_incl_scan((uint32_t)v);
+  if ((threadIdx.x & 63) == 63) s[w] = incl;
+  lds_barrier();
+  int off = incl - v;
+  for (int i = 0; i < w; ++i) off += s[i];
+  lds_barrier();
+  return off;
+}
+
 __global__ __launch_bounds__(256) void vs_centres_kernel(AttnArgs a, BhList L, int ND) {
+  __shared__ uint32_t s_bits[kCentreLdsWords];
+  __shared__ int32_t s_starts[kCentreLdsWords / 2 + 8];  // run starts of one chunk of words
+  __shared__ uint8_t s_cb[kCentreLdsWords + 8];          // a centre in 32 positions x, when they fit
   const int bh = L.bh[blockIdx.x];
-  const uint32_t* sp = a.sbits + (size_t)bh * a.sw;         // padded: two zero words first
-  const uint32_t* sb = sp + 2;                              // unpadded view
+  const uint32_t* sb = a.sbits + (size_t)bh * a.sw + 2;     // unpadded view (two zero words before it)
   uint32_t* cb = a.cbits + (size_t)bh * a.cw;
   int32_t* cl = a.clist + (size_t)bh * a.ccap * 4;
   int32_t* cle = a.cle + (size_t)bh * a.ccap;
-  __shared__ int s_wave[4];
-  __shared__ int s_base;
+  __shared__ int s_scan[4];
   __shared__ int s_prefix;
-  if (threadIdx.x == 0) {
-    s_base = 0;
-    s_prefix = 1;
-  }
+  if (threadIdx.x == 0) s_prefix = 1;
   __syncthreads();
   {
     const int nc = min(a.cols_count[bh], a.cols_cap), nd = min(a.diags_count[bh], a.diags_cap);
@@ -197,69 +223,93 @@ __global__ __launch_bounds__(256) void vs_centres_kernel(AttnArgs a, BhList L, i
       a.win[2 * bh + 1] = nc;
     }
   }
-  const int w = threadIdx.x >> 6;
+  // a window head runs on whole tiles and never reads its centres
+  if (s_prefix) return;
   const int nwords = (a.Nk + 31) / 32;
-  for (int x0 = 0; x0 < nwords; x0 += 256) {
-    const int x = x0 + threadIdx.x;
-    // the run start in word x, if any (two run starts are more than 63 apart)
-    int start = -1;
-    if (x < nwords) {
-      uint32_t m = sb[x];
-      if (m) {
-        int last = -1000;
-        for (int y = max(0, x - 2); y < x; ++y)
-          if (sb[y]) last = 32 * y + 31 - __builtin_clz(sb[y]);
-        while (m) {
-          const int o = 32 * x + __builtin_ctz(m);
-          if (o - last > 63) { start = o; break; }
-          last = o;
-          m &= m - 1;
+  const bool in_lds = nwords <= kCentreLdsWords;          // then ND <= kCentreLdsWords + 1
+  if (in_lds) {
+    for (int i = threadIdx.x; i < nwords; i += 256) s_bits[i] = sb[i];
+    for (int i = threadIdx.x; i < ND; i += 256) s_cb[i] = 0;
+  }
+  __syncthreads();
+  auto centres = [&](const auto& word) {
+    int base = 0;                                      // centres written so far
+    for (int c0 = 0; c0 < nwords; c0 += kCentreLdsWords) {
+      const int c1 = min(nwords, c0 + kCentreLdsWords);
+      // 1. the run starts of words [c0, c1), ascending: a word's lowest set bit
+      // o with none of the 63 offsets before it selected (any later set bit of
+      // a word has one less than 32 before it)
+      int nst = 0;
+      for (int x0 = c0; x0 < c1; x0 += 256) {
+        const int x = x0 + threadIdx.x;
+        bool st = false;
+        int o = 0;
+        if (x < c1) {
+          const uint32_t m = word(x);
+          if (m) {
+            o = 32 * x + __builtin_ctz(m);
+            const uint64_t prev = ((uint64_t)word(x - 1) << 32) | word(x - 2);   // offsets 32x - 64 .. 32x - 1
+            st = (prev >> ((o & 31) + 1)) == 0;
+          }
         }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(st);
+        const int wv = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) s_scan[wv] = __popcll(bal);
+        lds_barrier();
+        int pos = nst;
+        for (int i = 0; i < wv; ++i) pos += s_scan[i];
+        if (st) s_starts[pos + (int)ballot_rank(bal)] = o;
+        nst += s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+        lds_barrier();
+      }
+      // 2. one run start per thread: count its centres, place them, write them
+      for (int r0 = 0; r0 < nst; r0 += 256) {
+        const int i = r0 + threadIdx.x;
+        const int st = i < nst ? s_starts[i] : -1;
+        int cnt = 0;
+        if (st >= 0) follow_run(word, st, [&](int) { ++cnt; });
+        int off = base + block_excl_scan(cnt, s_scan);
+        if (st >= 0) {
+          follow_run(word, st, [&](int c) {
+            // the 64 diagonal bits of offsets [c - 32, c + 31]
+            const int wi = (c >> 5) - 1, sh = c & 31;
+            const uint64_t lo = ((uint64_t)word(wi + 1) << 32) | word(wi);
+            const uint64_t win = sh == 0 ? lo : (lo >> sh) | ((uint64_t)word(wi + 2) << (64 - sh));
+            u32x4 e = {(uint32_t)c, (uint32_t)win, (uint32_t)(win >> 32), 0u};
+            *(u32x4*)(cl + 4 * (size_t)off) = e;
+            cb[c >> 5] = 1u << (c & 31);                    // one centre per word at most
+            if (in_lds) s_cb[c >> 5] = 1;
+            ++off;
+          });
+        }
+        // the next round starts after the last centre of this one
+        if (threadIdx.x == 255) s_scan[0] = off;
+        lds_barrier();
+        base = s_scan[0];
+        lds_barrier();
       }
     }
-    int cnt = 0;
-    if (start >= 0) follow_run(sb, nwords, start, [&](int) { ++cnt; });
-    // exclusive prefix of the counts over the workgroup
-    const uint32_t incl = wave_incl_scan((uint32_t)cnt);
-    if ((threadIdx.x & 63) == 63) s_wave[w] = (int)incl;
-    __syncthreads();
-    int off = s_base + (int)incl - cnt;
-    for (int i = 0; i < w; ++i) off += s_wave[i];
-    if (start >= 0) {
-      follow_run(sb, nwords, start, [&](int c) {
-        const int i = (c >> 5) + 1, s = c & 31;               // padded word holding offset c - 32
-        const uint64_t lo = ((uint64_t)sp[i + 1] << 32) | sp[i];
-        const uint64_t win = s == 0 ? lo : (lo >> s) | ((uint64_t)sp[i + 2] << (64 - s));
-        int32_t* e = cl + 4 * (size_t)off;
-        e[0] = c;
-        e[1] = (int32_t)(uint32_t)win;
-        e[2] = (int32_t)(uint32_t)(win >> 32);
-        e[3] = 0;
-        cb[c >> 5] = 1u << (c & 31);                            // one centre per word at most
-        ++off;
-      });
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    __syncthreads();
+    return base;
+  };
+  int total;
+  if (in_lds) {
+    total = centres([&](int i) -> uint32_t { return (i >= 0 && i < nwords) ? s_bits[i] : 0u; });
+  } else {
+    total = centres([&](int i) -> uint32_t { return (i >= 0 && i < nwords) ? sb[i] : 0u; });
+    __syncthreads();                                    // the global centre bitmap is read back below
   }
-  // prefix counts per 32 positions (the bitmap holds at most one centre per word)
-  if (threadIdx.x == 0) s_prefix = 0;
-  __syncthreads();
-  for (int x0 = 0; x0 < ND; x0 += 256) {
-    const int x = x0 + threadIdx.x;
-    const bool in = x < ND && cb[x] != 0u;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(in);
-    if ((threadIdx.x & 63) == 0) s_wave[w] = __popcll(bal);
-    __syncthreads();
-    int off = s_prefix;
-    for (int i = 0; i < w; ++i) off += s_wave[i];
-    if (x < ND) cle[x] = off + (int)ballot_rank(bal) + (in ? 1 : 0);
-    __syncthreads();
-    if (threadIdx.x == 0) s_prefix += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    __syncthreads();
+  // prefix counts per 32 positions (at most one centre per 32 positions): each
+  // thread counts the centres of its range, one scan, then fills it
+  const int pc = (ND + 255) / 256;
+  const int c_lo = threadIdx.x * pc, c_hi = min(ND, c_lo + pc);
+  int n_own = 0;
+  for (int x = c_lo; x < c_hi; ++x) n_own += (in_lds ? s_cb[x] != 0 : cb[x] != 0u) ? 1 : 0;
+  int run = block_excl_scan(n_own, s_scan);
+  for (int x = c_lo; x < c_hi; ++x) {
+    run += (in_lds ? s_cb[x] != 0 : cb[x] != 0u) ? 1 : 0;
+    cle[x] = run;
   }
-  if (threadIdx.x == 0) a.ccount[bh] = s_base;
+  if (threadIdx.x == 0) a.ccount[bh] = total;
 }
 
 // ---------------------------------------------------------------- main kernel
