@@ -59,6 +59,11 @@ constexpr int GCAP = 2048;   // gathered columns staged per round
 
 enum { M_NONE = 0, M_CAUSAL = 1, M_WIN = 2, M_GATHER = 3, M_SKIP = 4 };
 
+// Entries of the schedule's head table: b * H + h, with two flag bits for the
+// pairs of block heads (see launch_attention).
+constexpr int kPairBit = 0x4000, kParityBit = 0x2000, kHeadMask = 0x1FFF;
+static_assert(kMaxHeadTable <= kHeadMask + 1, "head index and flags overlap");
+
 struct Sched {
   int nq;                       // number of queues
   int T2;                       // query-tile pairs per head
@@ -569,14 +574,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       if (itn >= nitems) break;
 
       Item it;
-      it.bh = arg_i16(sc.heads, sc.qstart[g] + itn % nh);
+      const int he = arg_i16(sc.heads, sc.qstart[g] + itn % nh);
+      const bool paired = (he & kPairBit) != 0;     // one query tile of heads bh0, bh0 + 1
+      const int bh0 = he & kHeadMask;
+      it.bh = bh0 + (paired ? ih : 0);               // this wave's head
       const int b = it.bh / a.H, h = it.bh % a.H;
       it.kvh = h / rep;
       it.kind = arg_i8(a.kind, h);
       const int p = sc.T2 - 1 - itn / nh;
-      const int r0 = p * 2 * TQ;
+      const int r0 = p * 2 * TQ + (paired && (he & kParityBit) ? TQ : 0);
       it.P0 = r0 + a.q_offset;
-      it.last_pos = min(a.Nq, r0 + 2 * TQ) - 1 + a.q_offset;
+      it.last_pos = min(a.Nq, r0 + (paired ? TQ : 2 * TQ)) - 1 + a.q_offset;
       it.tq1 = it.P0 / TK + 1;
       it.ngather = 0;
       it.per = 1;
@@ -587,8 +595,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       const uint16_t* vbp = a.v + ((size_t)(b * a.Hkv + it.kvh) * a.Nk) * 128;
       const uint16_t* qbp = a.q + ((size_t)it.bh * a.Nq) * 128;
 
-      const int qrow = r0 + TQ * ih + 32 * wr + qn;
-      const int P0w = it.P0 + TQ * ih;                // first position of this wave's query tile
+      const int qrow = r0 + (paired ? 0 : TQ * ih) + 32 * wr + qn;
+      const int P0w = it.P0 + (paired ? 0 : TQ * ih); // first position of this wave's query tile
       const int R0w = P0w + 32 * wr;                   // position of this wave's first row
       const int iq = R0w + qn;                         // absolute position of this lane's row
       const bool row_ok = qrow < a.Nq;
@@ -1020,10 +1028,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
       } else if (it.kind == 2) {
         it.per = a.block / TK;
         const int I0 = it.P0 / a.block;
-        it.l0 = a.bidx + ((size_t)it.bh * a.nqb + I0) * a.bcap;
-        it.n0 = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I0), a.bcap);
+        // A pair's second query tile of the last pair of tiles can lie past the
+        // last query (an odd number of tiles): then the item has no rows and
+        // reads no list (its query block would be past the heads' lists).
+        const bool has_rows = r0 < a.Nq;
+        it.l0 = a.bidx + ((size_t)bh0 * a.nqb + (has_rows ? I0 : 0)) * a.bcap;
+        it.n0 = has_rows ? min(ldc(a.bcount, (size_t)bh0 * a.nqb + I0), a.bcap) : 0;
         it.l1 = it.l0;
-        if (it.per == 1 && I0 + 1 < a.nqb && r0 + TQ < a.Nq) {
+        if (paired) {
+          // the second head's list of the same query block
+          it.l1 = a.bidx + ((size_t)(bh0 + 1) * a.nqb + (has_rows ? I0 : 0)) * a.bcap;
+          it.n1 = has_rows ? min(ldc(a.bcount, (size_t)(bh0 + 1) * a.nqb + I0), a.bcap) : 0;
+        } else if (it.per == 1 && I0 + 1 < a.nqb && r0 + TQ < a.Nq) {
           it.l1 = a.bidx + ((size_t)it.bh * a.nqb + I0 + 1) * a.bcap;
           it.n1 = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I0 + 1), a.bcap);
         }
@@ -1321,18 +1337,35 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
   // through that XCD's L2.  Groups are placed longest first into the
   // least-loaded queue; within a queue, consecutive items are the group's
   // heads at the same query rows.
-  struct HC { double cost; int bh; };
+  // Block heads with 64-key blocks come in pairs of neighbouring heads of one
+  // KV group where they can: an item of a pair is one query tile of both heads
+  // (waves 0-1 the first head, 2-3 the second), which merges the two heads'
+  // lists of the same query block, rather than two query tiles of one head.
+  // Heads that share their K choose many of the same key blocks, so more of
+  // the merged tiles serve all four waves.  A pair is listed twice, once per
+  // parity of its query tiles, so that every entry still has T2 items.
+  struct HC { double cost; int bh; int enc; };
   std::vector<HC> heads;
+  const int rep_h = a.H / a.Hkv;
   for (int b = 0; b < a.B; ++b)
     for (int h = 0; h < a.H; ++h) {
       const int kd = a.kind[h];
       if (kd < 0 || kd > 2) continue;
+      const bool pair = kd == 2 && a.block == TK && h + 1 < a.H && a.kind[h + 1] == 2 && h / rep_h == (h + 1) / rep_h;
+      if (pair) {
+        const double per = std::min<double>(a.bcap * (a.block / TK), 0.5 * a.Nk / TK);
+        const int bh = b * a.H + h;
+        heads.push_back({per * T, bh, bh | kPairBit});
+        heads.push_back({per * T, bh, bh | kPairBit | kParityBit});
+        ++h;
+        continue;
+      }
       double per;
       if (kd == 0) per = 0.5 * (a.Nk / (double)TK);
       else if (kd == 2 && a.block < TK) per = std::min<double>(a.bcap * (32.0 / a.block), 0.5 * a.Nk / TK);
       else if (kd == 2) per = std::min<double>(a.bcap * (a.block / TK), 0.5 * a.Nk / TK);
       else per = std::min<double>(0.5 * a.Nk / TK, 2.0 * a.diags_cap / TK + 1 + a.cols_cap / (double)TK);
-      heads.push_back({per * T, b * a.H + h});
+      heads.push_back({per * T, b * a.H + h, b * a.H + h});
     }
   if ((e = launch_token_attention(a, st)) != hipSuccess) return e;
   if (heads.empty()) return hipSuccess;
@@ -1343,7 +1376,7 @@ hipError_t launch_attention(AttnArgs& a, void* ws, hipStream_t st) {
     const int key = (x.bh / a.H) * a.Hkv + (x.bh % a.H) / rep;   // b * Hkv + kv head
     if (groups.empty() || groups.back().key != key) groups.push_back({0.0, key, {}});
     groups.back().cost += x.cost;
-    groups.back().bh.push_back(x.bh);
+    groups.back().bh.push_back(x.enc);
   }
   std::stable_sort(groups.begin(), groups.end(), [](const GC& x, const GC& y) { return x.cost > y.cost; });
   Sched sc;

@@ -160,3 +160,15 @@ def test_vertical_slash_constructed_sets(Nk, Nq):
     for (b, h) in sets:
         ref_o, ref_l = oracle_attention_rows(w, sets, b, h, rows)
         assert_attention_close(o[b, h], lse[b, h], ref_o, ref_l, f"constructed sets h={h}")
+
+
+@pytest.mark.parametrize("Nk", [1000, 1345])
+def test_block_head_pairs(Nk):
+    """Neighbouring block heads of one KV group (blocks of 64) run as pairs:
+    an item is one query tile of both heads, over the merge of their lists.
+    Batch 2, GQA 8 / 2, an odd number of query tiles (the last pair of tiles
+    has no second tile), a head whose neighbour is not a block head, and
+    top-k and threshold rules side by side."""
+    heads = [blk("topk", 5, True), blk("thresh"), blk("topk", 3), dense(),
+             blk("thresh"), blk("topk", 7, True), vs(64, 20, 40), blk("topk", 2)]
+    run_and_check(workload(80 + Nk, 2, 8, 2, Nk, heads), f"block pairs N={Nk}")
