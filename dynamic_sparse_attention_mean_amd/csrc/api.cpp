@@ -245,15 +245,19 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
   if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
   if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
   if (!block_size_ok(block)) return fail(DSA_ERR_UNSUPPORTED, "block %d (16, 32, 64 or 128)", block);
-  if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "the block rule needs q_offset == 0");
+  if (shape->q_offset % block != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "the block rule needs q_offset (%d) to be a multiple of the block (%d)",
+                shape->q_offset, block);
   if (mode != DSA_SELECT_TOPK && mode != DSA_SELECT_THRESHOLD) return fail(DSA_ERR_INVALID_ARG, "mode %d", mode);
   if (mode == DSA_SELECT_TOPK && topk < 0) return fail(DSA_ERR_INVALID_ARG, "topk < 0");
   if (mode == DSA_SELECT_THRESHOLD && !(log_alpha <= 0.f)) return fail(DSA_ERR_INVALID_ARG, "log_alpha must be <= 0");
   if (out.block != block) return fail(DSA_ERR_INVALID_ARG, "out.block != block");
   if (!out.idx || !out.count) return fail(DSA_ERR_INVALID_ARG, "index set pointers are null");
   const int nqb = (shape->q_len + block - 1) / block, nkb = (shape->kv_len + block - 1) / block;
+  const int qb0 = shape->q_offset / block;          // the chunk's first query block, absolute
   const int forced = (force_first ? 1 : 0) + (force_diag ? 1 : 0);
-  const int need_cap = mode == DSA_SELECT_TOPK ? std::min(nqb, topk + forced) : nqb;
+  // the last query block sees key blocks [0, qb0 + nqb)
+  const int need_cap = mode == DSA_SELECT_TOPK ? std::min(qb0 + nqb, topk + forced) : qb0 + nqb;
   if (out.cap < need_cap) return fail(DSA_ERR_INVALID_ARG, "out.cap %d < %d", out.cap, need_cap);
   const size_t need = ws_block(shape, n_heads, block);
   if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -283,15 +287,15 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
     return st;
   const float scale = (float)(1.0 / std::sqrt(128.0));
   if (on_chip)
-    return hip_status(launch_block_index(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, hl, scale, mode,
-                                         topk, log_alpha, force_first, force_diag, out.idx, out.count, out.cap,
+    return hip_status(launch_block_index(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, qb0, hl, scale,
+                                         mode, topk, log_alpha, force_first, force_diag, out.idx, out.count, out.cap,
                                          scores, s),
                       "build_index_block: scores + select");
-  if ((st = hip_status(launch_block_scores(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, hl, scale,
+  if ((st = hip_status(launch_block_scores(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, qb0, hl, scale,
                                            sc, s),
                        "build_index_block: scores")))
     return st;
-  return hip_status(launch_block_select(sc, shape->batch, shape->heads, nqb, nkb, hl, mode, topk, log_alpha,
+  return hip_status(launch_block_select(sc, shape->batch, shape->heads, nqb, nkb, qb0, hl, mode, topk, log_alpha,
                                         force_first, force_diag, out.idx, out.count, out.cap, s),
                     "build_index_block: select");
 }
@@ -458,7 +462,9 @@ dsa_status prepare_attn(const dsa_shape* shape, const void* q, const void* k, co
   if (use[DSA_PATTERN_BLOCK]) {
     if (!blk || !blk->idx || !blk->count || blk->cap < 1) return fail(DSA_ERR_INVALID_ARG, "block heads need a block index set");
     if (!block_size_ok(blk->block)) return fail(DSA_ERR_UNSUPPORTED, "block size %d", blk->block);
-    if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "block heads need q_offset == 0");
+    if (shape->q_offset % blk->block != 0)
+      return fail(DSA_ERR_UNSUPPORTED, "block heads need q_offset (%d) to be a multiple of the block (%d)",
+                  shape->q_offset, blk->block);
   }
   if (use[DSA_PATTERN_TOKEN]) {
     if (!tok || !tok->idx || !tok->count || tok->cap < 1) return fail(DSA_ERR_INVALID_ARG, "token heads need a token index set");
@@ -475,6 +481,7 @@ dsa_status prepare_attn(const dsa_shape* shape, const void* q, const void* k, co
   if (use[DSA_PATTERN_BLOCK]) {
     a.bidx = blk->idx; a.bcount = blk->count; a.bcap = blk->cap; a.block = blk->block;
     a.nqb = (shape->q_len + blk->block - 1) / blk->block;
+    a.qb0 = shape->q_offset / blk->block;
   }
   if (use[DSA_PATTERN_TOKEN]) {
     a.tidx = tok->idx; a.tcount = tok->count; a.tcap = tok->cap;

@@ -911,10 +911,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           const int nq_item = 2 * TQ / a.block;
           const int I0 = it.P0 / a.block;
           for (int q = w; q < nq_item; q += 4) {
-            const int I = I0 + q;
-            if (I >= a.nqb || I * a.block > it.last_pos) continue;
-            const int32_t* li = a.bidx + ((size_t)it.bh * a.nqb + I) * a.bcap;
-            const int n = min(ldc(a.bcount, (size_t)it.bh * a.nqb + I), a.bcap);
+            const int I = I0 + q;                // absolute query block
+            const int Ir = I - a.qb0;            // its row of the chunk's lists
+            if (Ir >= a.nqb || I * a.block > it.last_pos) continue;
+            const int32_t* li = a.bidx + ((size_t)it.bh * a.nqb + Ir) * a.bcap;
+            const int n = min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ir), a.bcap);
             for (int x = l; x < n; x += 64) {
               const int J = li[x];
               const int u = J >> sh;
@@ -980,12 +981,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         __syncthreads();                         // every wave has read the item number
         const uint32_t wslot = (uint32_t)(w * SLOT);
         if (R0w <= it.last_pos) {
-          const int Ia = R0w / a.block;
-          const int32_t* la = a.bidx + ((size_t)it.bh * a.nqb + Ia) * a.bcap;
-          const int na = min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ia), a.bcap);
-          const bool two = a.block == 16 && Ia + 1 < a.nqb && R0w + 16 < a.Nq;   // rows 16-31: the next query block
-          const int32_t* lb = two ? a.bidx + ((size_t)it.bh * a.nqb + Ia + 1) * a.bcap : la;
-          const int nb = two ? min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ia + 1), a.bcap) : 0;
+          const int Ir = R0w / a.block - a.qb0;  // the list row of the wave's first query block
+          const int32_t* la = a.bidx + ((size_t)it.bh * a.nqb + Ir) * a.bcap;
+          const int na = min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ir), a.bcap);
+          // rows 16-31: the next query block
+          const bool two = a.block == 16 && Ir + 1 < a.nqb && R0w + 16 < a.Nq + a.q_offset;
+          const int32_t* lb = two ? a.bidx + ((size_t)it.bh * a.nqb + Ir + 1) * a.bcap : la;
+          const int nb = two ? min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ir + 1), a.bcap) : 0;
           const int sh = a.block == 16 ? 1 : 0;   // list entry J lies in 32-key unit J >> sh
           constexpr int NONE = 0x7fffffff;
           int ia = 0, ib = 0;
@@ -1027,7 +1029,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
         it.kind = 4;                             // no tile steps for this item
       } else if (it.kind == 2) {
         it.per = a.block / TK;
-        const int I0 = it.P0 / a.block;
+        const int I0 = it.P0 / a.block - a.qb0;  // the list row of the item's first query block
         // A pair's second query tile of the last pair of tiles can lie past the
         // last query (an odd number of tiles): then the item has no rows and
         // reads no list (its query block would be past the heads' lists).

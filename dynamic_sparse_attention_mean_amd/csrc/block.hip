@@ -49,16 +49,17 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// Block scores S[I][J] = qbar_I . kbar_J * scale (J <= I), 64x64 tile per
-// workgroup, four waves of 32x32 each, v_mfma_f32_32x32x16_bf16.
+// Block scores S[I][J] = qbar_I . kbar_J * scale (J <= qb0 + I: row I is the
+// chunk's query block I, absolute block qb0 + I), 64x64 tile per workgroup,
+// four waves of 32x32 each, v_mfma_f32_32x32x16_bf16.
 __global__ __launch_bounds__(256) void block_scores_kernel(const uint16_t* __restrict__ qbar,
                                                            const uint16_t* __restrict__ kbar, int H, int Hkv,
-                                                           int nqb, int nkb, HeadList heads, float scale,
+                                                           int nqb, int nkb, int qb0, HeadList heads, float scale,
                                                            float* __restrict__ scores) {
   const int J0 = blockIdx.x * 64, I0 = blockIdx.y * 64;
   const int hi = blockIdx.z % heads.n, b = blockIdx.z / heads.n;
-  if (J0 > I0 + 63) {
-    // wholly above the diagonal: -inf (selection reads only J <= I)
+  if (J0 > qb0 + I0 + 63) {
+    // wholly above the diagonal: -inf (selection reads only J <= qb0 + I)
     float* sp = scores + ((size_t)(b * heads.n + hi) * nqb) * nkb;
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
       const int I = I0 + (e >> 6), J = J0 + (e & 63);
@@ -90,36 +91,38 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const uint16_t* __res
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int I = I0 + 32 * wi + 8 * (v >> 2) + 4 * hh + (v & 3);
-    if (I < nqb && J < nkb) sp[(size_t)I * nkb + J] = (J <= I) ? acc[v] * scale : -INFINITY;
+    if (I < nqb && J < nkb) sp[(size_t)I * nkb + J] = (J <= qb0 + I) ? acc[v] * scale : -INFINITY;
   }
 }
 
-// One workgroup per (query block I, listed head, batch).
+// One workgroup per (query block I of the chunk, listed head, batch); its
+// absolute block is Ia = qb0 + I.
 __global__ __launch_bounds__(256) void block_select_kernel(const float* __restrict__ scores, int H, int nqb,
-                                                           int nkb, HeadList heads, int mode, int topk,
+                                                           int nkb, int qb0, HeadList heads, int mode, int topk,
                                                            float log_alpha, int force_first, int force_diag,
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                                            int cap) {
   __shared__ SelectSmem<256> sm;
   const int I = blockIdx.x, hi = blockIdx.y, b = blockIdx.z;
+  const int Ia = qb0 + I;
   const int h = heads.h[hi];
   const float* row = scores + (((size_t)(b * heads.n + hi) * nqb) + I) * nkb;
   int32_t* out = idx + (((size_t)(b * H + h) * nqb) + I) * cap;
   int n;
   if (mode == 0) {
-    // candidates [0, I] minus the forced blocks; those are the smallest (0) and
-    // largest (I) indices, so the merged list is [0] + selected + [I].
-    n = select_topk<256>(row, 0, I + 1, force_first ? 0 : -1, force_diag ? I : -1, topk,
+    // candidates [0, Ia] minus the forced blocks; those are the smallest (0) and
+    // largest (Ia) indices, so the merged list is [0] + selected + [Ia].
+    n = select_topk<256>(row, 0, Ia + 1, force_first ? 0 : -1, force_diag ? Ia : -1, topk,
                          out + (force_first ? 1 : 0), sm);
     if (threadIdx.x == 0) {
       int c = n;
       if (force_first) { out[0] = 0; ++c; }
-      if (force_diag && !(force_first && I == 0)) { out[c] = I; ++c; }
+      if (force_diag && !(force_first && Ia == 0)) { out[c] = Ia; ++c; }
       count[(size_t)(b * H + h) * nqb + I] = c;
     }
   } else {
-    // threshold over all J <= I; forced blocks are added when not already kept
-    n = select_threshold<256>(row, 0, I + 1, log_alpha, out, 0, sm, nullptr);
+    // threshold over all J <= Ia; forced blocks are added when not already kept
+    n = select_threshold<256>(row, 0, Ia + 1, log_alpha, out, 0, sm, nullptr);
     if (threadIdx.x == 0) {
       int c = n;
       if (force_first && (c == 0 || out[0] != 0)) {
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
         out[0] = 0;
         ++c;
       }
-      if (force_diag && (c == 0 || out[c - 1] != I)) { out[c] = I; ++c; }
+      if (force_diag && (c == 0 || out[c - 1] != Ia)) { out[c] = Ia; ++c; }
       count[(size_t)(b * H + h) * nqb + I] = c;
     }
   }
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
 // section; "FlashPrefill" section 2.1, scoring fused with the block search).
 //
 // A workgroup of 16 waves owns a strip of R consecutive query blocks of one
-// head.  It computes their scores S[I][J] (J < I0 + R) on
+// head (of a prefill chunk whose first query block is absolute block qb0).  It
+// computes their scores S[I][J] (J < qb0 + I0 + R) on
 // v_mfma_f32_16x16x32_bf16 into LDS (A = 16 pooled keys, B = the strip's
 // pooled queries), then wave r selects row I0 + r from LDS: the radix top-k
 // (four 8-bit digits of the order-preserving key, a per-wave histogram) or the
@@ -184,7 +188,7 @@ __device__ __forceinline__ void strip_scores(const uint16_t* __restrict__ qp, co
 
 __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
     const uint16_t* __restrict__ qbar, const uint16_t* __restrict__ kbar, int H, int Hkv, int nqb, int nkb,
-    HeadList heads, float scale, int R, int stride, int mode, int topk, float log_alpha, int force_first,
+    int qb0, HeadList heads, float scale, int R, int stride, int mode, int topk, float log_alpha, int force_first,
     int force_diag, int32_t* __restrict__ idx, int32_t* __restrict__ count, int cap, float* __restrict__ scores_out) {
   __shared__ __align__(16) float s_sc[kBlockStripFloats];
   __shared__ uint32_t s_hist[FB_WAVES][256];
@@ -194,34 +198,35 @@ __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int rows = min(R, nqb - I0);
-  const int nk = min(nkb, I0 + rows);                  // keys any row of the strip sees: J < nk
+  const int nk = min(nkb, qb0 + I0 + rows);            // keys any row of the strip sees: J < nk
   const uint16_t* qp = qbar + ((size_t)(b * H + h) * nqb) * 128;
   const uint16_t* kp = kbar + ((size_t)(b * Hkv + kvh) * nkb) * 128;
   strip_scores(qp, kp, I0, rows, nk, scale, stride, s_sc);
   __syncthreads();
 
   if (scores_out) {
-    // inspection copy of the strip: the full rows, -inf for J > I
+    // inspection copy of the strip: the full rows, -inf for J > qb0 + I
     for (int r = 0; r < rows; ++r) {
       float* dst = scores_out + (((size_t)(b * heads.n + hi) * nqb) + I0 + r) * nkb;
-      for (int J = tid; J < nkb; J += FB_THREADS) dst[J] = J <= I0 + r ? s_sc[r * stride + J] : -INFINITY;
+      for (int J = tid; J < nkb; J += FB_THREADS) dst[J] = J <= qb0 + I0 + r ? s_sc[r * stride + J] : -INFINITY;
     }
   }
   if (w >= rows) return;
 
-  // ---- selection of row I by wave w
+  // ---- selection of row I (absolute query block Ia) by wave w
   const int I = I0 + w;
+  const int Ia = qb0 + I;
   const float* sr = s_sc + w * stride;
   int32_t* out = idx + (((size_t)(b * H + h) * nqb) + I) * cap;
   const int ex0 = force_first ? 0 : -1;
-  const int ex1 = force_diag ? I : -1;
+  const int ex1 = force_diag ? Ia : -1;
   uint32_t T = 0u;
   int need_eq = 0;
   bool all = false, none = false;
   float cut = 0.f;
   if (mode == 0) {
     const int nex = (ex0 == 0 ? 1 : 0) + ((ex1 >= 0 && ex1 != ex0) ? 1 : 0);
-    const int ncand = I + 1 - nex;
+    const int ncand = Ia + 1 - nex;
     none = topk <= 0 || ncand <= 0;
     all = !none && topk >= ncand;
     if (!none && !all) {
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) hist[l + 64 * i] = 0u;
         wave_lds_sync();
-        for (int j = l; j <= I; j += 64) {
+        for (int j = l; j <= Ia; j += 64) {
           if (j == ex0 || j == ex1) continue;
           const uint32_t key = f32_order_key(sr[j]);
           if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
@@ -267,16 +272,16 @@ __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
     }
   } else {
     float mx = -INFINITY;
-    for (int j = l; j <= I; j += 64) mx = fmaxf(mx, sr[j]);
+    for (int j = l; j <= Ia; j += 64) mx = fmaxf(mx, sr[j]);
     cut = wave_max(mx) + log_alpha;
   }
   // ordered compaction: forced blocks, then the selected ones (keys above T and
   // the lowest-indexed keys equal to T, or scores at or above the cut)
   int pos = 0, eqb = 0;
-  for (int j0 = 0; j0 <= I; j0 += 64) {
+  for (int j0 = 0; j0 <= Ia; j0 += 64) {
     const int j = j0 + l;
     bool take = false, e = false;
-    if (j <= I) {
+    if (j <= Ia) {
       if (j == ex0 || j == ex1) {
         take = true;
       } else if (mode == 0) {
@@ -448,7 +453,7 @@ int block_strip_rows(int nkb, int* stride) {
 }
 
 hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
-                              const HeadList& heads, float scale, int mode, int topk, float log_alpha,
+                              int qb0, const HeadList& heads, float scale, int mode, int topk, float log_alpha,
                               int force_first, int force_diag, int32_t* idx, int32_t* count, int cap,
                               float* scores, hipStream_t st) {
   if (heads.n == 0) return hipSuccess;
@@ -456,7 +461,8 @@ hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B,
   const int R = block_strip_rows(nkb, &stride);
   if (R < 1) return hipErrorInvalidValue;
   dim3 grid((nqb + R - 1) / R, heads.n, B);
-  hipLaunchKernelGGL(block_index_kernel, grid, dim3(FB_THREADS), 0, st, qbar, kbar, H, Hkv, nqb, nkb, heads, scale, R,
+  hipLaunchKernelGGL(block_index_kernel, grid, dim3(FB_THREADS), 0, st, qbar, kbar, H, Hkv, nqb, nkb, qb0, heads,
+                     scale, R,
                      stride, mode, topk, log_alpha, force_first, force_diag, idx, count, cap, scores);
   return hipGetLastError();
 }
@@ -494,18 +500,20 @@ hipError_t launch_pool(const uint16_t* src, int B, int Hs, int N, const HeadList
 }
 
 hipError_t launch_block_scores(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
-                               const HeadList& heads, float scale, float* scores, hipStream_t st) {
+                               int qb0, const HeadList& heads, float scale, float* scores, hipStream_t st) {
   if (heads.n == 0) return hipSuccess;
   dim3 grid((nkb + 63) / 64, (nqb + 63) / 64, heads.n * B);
-  hipLaunchKernelGGL(block_scores_kernel, grid, dim3(256), 0, st, qbar, kbar, H, Hkv, nqb, nkb, heads, scale, scores);
+  hipLaunchKernelGGL(block_scores_kernel, grid, dim3(256), 0, st, qbar, kbar, H, Hkv, nqb, nkb, qb0, heads, scale,
+                     scores);
   return hipGetLastError();
 }
 
-hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb, const HeadList& heads, int mode,
-                               int topk, float log_alpha, int force_first, int force_diag, int32_t* idx,
+hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb, int qb0, const HeadList& heads,
+                               int mode, int topk, float log_alpha, int force_first, int force_diag, int32_t* idx,
                                int32_t* count, int cap, hipStream_t st) {
   if (heads.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_select_kernel, dim3(nqb, heads.n, B), dim3(256), 0, st, scores, H, nqb, nkb, heads, mode,
+  hipLaunchKernelGGL(block_select_kernel, dim3(nqb, heads.n, B), dim3(256), 0, st, scores, H, nqb, nkb, qb0, heads,
+                     mode,
                      topk, log_alpha, force_first, force_diag, idx, count, cap);
   return hipGetLastError();
 }

@@ -26,9 +26,10 @@ hipError_t launch_pool(const uint16_t* src, int B, int Hs, int N, const HeadList
                        int block, uint16_t* dst, hipStream_t st);
 
 // ------------------------------------------------------------ block scores
-// scores[b][h][I][J] = qbar[b][h][I] . kbar[b][kvh][J] * scale for J <= I (fp32).
+// scores[b][h][I][J] = qbar[b][h][I] . kbar[b][kvh][J] * scale for J <= qb0 + I
+// (fp32; query block I of a chunk is absolute block qb0 + I).
 hipError_t launch_block_scores(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv,
-                               int nqb, int nkb, const HeadList& heads, float scale, float* scores,
+                               int nqb, int nkb, int qb0, const HeadList& heads, float scale, float* scores,
                                hipStream_t st);
 
 // --------------------------------------------- fused block scores + select
@@ -39,7 +40,7 @@ hipError_t launch_block_scores(const uint16_t* qbar, const uint16_t* kbar, int B
 constexpr int kBlockStripFloats = 32768;   // 128 KB of fp32 scores per workgroup
 int block_strip_rows(int nkb, int* stride);
 hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
-                              const HeadList& heads, float scale, int mode, int topk, float log_alpha,
+                              int qb0, const HeadList& heads, float scale, int mode, int topk, float log_alpha,
                               int force_first, int force_diag, int32_t* idx, int32_t* count, int cap,
                               float* scores, hipStream_t st);
 
@@ -58,7 +59,7 @@ hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, i
 // ---------------------------------------------------------------- select
 // Per listed head and query block I: block selection over scores row I
 // (rows too long to keep on chip: the scores go through the workspace).
-hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb,
+hipError_t launch_block_select(const float* scores, int B, int H, int nqb, int nkb, int qb0,
                                const HeadList& heads, int mode, int topk, float log_alpha,
                                int force_first, int force_diag, int32_t* idx, int32_t* count,
                                int cap, hipStream_t st);
@@ -118,6 +119,7 @@ struct AttnArgs {
                                      // cols = [0, sink), diags = [0, window) (else window = -1)
   // Block sets
   const int32_t* bidx; const int32_t* bcount; int bcap, block, nqb;
+  int qb0;                           // lists are per query block of the chunk; its first is absolute block qb0
   // Token sets
   const int32_t* tidx; const int32_t* tcount; int tcap;
   // Scheduling

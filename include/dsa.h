@@ -93,10 +93,11 @@ typedef struct dsa_vs_index {
   int32_t  diags_cap;
 } dsa_vs_index;
 
-/* Block index set (device memory, caller-owned).  For query block I (absolute
- * positions [I*block, (I+1)*block)), idx[b][h][I][0 .. count[b][h][I]) are the
- * selected key blocks J <= I, ascending.  M(i) = { j <= p_i : j / block in
- * Sel(p_i / block) }.  Requires q_offset == 0; nqb = ceil(Nq / block). */
+/* Block index set (device memory, caller-owned).  Row I holds the chunk's
+ * query block I, absolute block Ia = q_offset / block + I (positions
+ * [Ia*block, (Ia+1)*block)): idx[b][h][I][0 .. count[b][h][I]) are its selected
+ * key blocks J <= Ia, ascending.  M(i) = { j <= p_i : j / block in Sel(p_i /
+ * block) }.  Requires q_offset to be a multiple of block; nqb = ceil(Nq / block). */
 typedef struct dsa_block_index {
   int32_t* idx;          /* [B, H, nqb, cap] */
   int32_t* count;        /* [B, H, nqb] */
@@ -162,16 +163,21 @@ dsa_status build_index_vs(const dsa_shape* shape, const void* q, const void* k,
  * K per block and keep important blocks; "FlashPrefill" section 2.1 mean keys,
  * section 2.2 threshold; MoBA's FlashMoBA top-k over key-block means).
  *   Qbar_I, Kbar_J = exact block means rounded to bf16 (round to nearest even);
- *   S[I, J] = Qbar_I . Kbar_J / sqrt(d) for J <= I;
- *   mode DSA_SELECT_TOPK: top-`topk` of J in [0, I] minus forced blocks;
+ *   query block I of a prefill chunk is absolute block Ia = q_offset / block + I
+ *   (its rows are the chunk's rows I * block ..; q_offset = 0 for a whole prompt);
+ *   S[I, J] = Qbar_I . Kbar_J / sqrt(d) for J <= Ia;
+ *   mode DSA_SELECT_TOPK: top-`topk` of J in [0, Ia] minus forced blocks;
  *   mode DSA_SELECT_THRESHOLD: J with S[I, J] >= max_J' S[I, J'] + log_alpha;
- *   then the union with block 0 (force_first) and block I (force_diag).
- * block in {16, 32, 64, 128}; q_offset must be 0; out.cap >= the largest count (top-k:
- * min(nqb, topk + forced); threshold: nqb).  Nullable outputs for inspection:
+ *   then the union with block 0 (force_first) and block Ia (force_diag).
+ * Lists hold absolute key blocks, one list per query block of the chunk (nqb =
+ * ceil(q_len / block) of them).  block in {16, 32, 64, 128}; q_offset must be a
+ * multiple of block (DSA_ERR_UNSUPPORTED otherwise); out.cap >= the largest count
+ * (top-k: min(qb0 + nqb, topk + forced); threshold: qb0 + nqb, with qb0 =
+ * q_offset / block).  Nullable outputs for inspection:
  * qbar ([B, H, nqb, d] bf16, indexed by head number, rows of listed heads
  * written), kbar ([B, Hkv, nkb, d] bf16, rows of the listed heads' KV heads
  * written) and scores ([B, n_heads, nqb, nkb] float in listed order, -inf for
- * J > I).  Workspace:
+ * J > Ia).  Workspace:
  * dsa_workspace_size(DSA_OP_BLOCK, {n_heads, block}). */
 dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* k,
                              const int32_t* heads, int32_t n_heads, int32_t block,

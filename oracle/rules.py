@@ -39,9 +39,12 @@ def block_means(x, block):
     return round_bf16(out)
 
 
-def block_scores(qbar, kbar, scale=None):
-    """S[I, J] = qbar_I . kbar_J * scale for J <= I, -inf above the diagonal.
+def block_scores(qbar, kbar, scale=None, q_block0=0):
+    """S[I, J] = qbar_I . kbar_J * scale for J <= q_block0 + I, -inf beyond.
 
+    Row I of qbar is absolute query block q_block0 + I: a prefill chunk whose
+    first query sits at q_offset = q_block0 * block pools its own rows, and its
+    block I sees the key blocks up to and including its own absolute block.
     The pages do not fix the scale; reading: 1/sqrt(d), as in attention.
     """
     qbar = np.asarray(qbar, dtype=np.float64)
@@ -50,7 +53,7 @@ def block_scores(qbar, kbar, scale=None):
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     s = (qbar @ kbar.T) * scale
     nq, nk = s.shape
-    causal = np.arange(nk)[None, :] <= np.arange(nq)[:, None]
+    causal = np.arange(nk)[None, :] <= np.arange(nq)[:, None] + q_block0
     return np.where(causal, s, -np.inf)
 
 
@@ -84,17 +87,21 @@ def threshold_rule(scores, candidates, log_alpha):
     return np.sort(cand[keep])
 
 
-def select_blocks(S, mode, k=0, log_alpha=-np.log(20.0), force_first=False, force_diag=False):
-    """Selected key blocks Sel(I) for every query block I of a score matrix.
+def select_blocks(S, mode, k=0, log_alpha=-np.log(20.0), force_first=False, force_diag=False, q_block0=0):
+    """Selected key blocks Sel(I) for every absolute query block I.
 
-    Candidates are the block-causal J <= I.  Forced blocks (first block 0 and
-    the diagonal block I) are added outside the budget: top-k runs over the
-    other candidates, the threshold over all of J <= I.  Reading for the
-    forced blocks under the threshold rule: parity unpinned beyond brute force
-    (the pages only pair forced blocks with top-k).
+    Row r of S is absolute query block I = q_block0 + r (block_scores of a
+    prefill chunk).  Candidates are the block-causal J <= I.  Forced blocks
+    (first block 0 and the diagonal block I) are added outside the budget:
+    top-k runs over the other candidates, the threshold over all of J <= I.
+    Reading for the forced blocks under the threshold rule: parity unpinned
+    beyond brute force (the pages only pair forced blocks with top-k).
+    The result is indexed by absolute query block; the q_block0 blocks before
+    the chunk hold empty lists.
     """
-    out = []
-    for I in range(S.shape[0]):
+    out = [np.zeros(0, dtype=np.int64) for _ in range(q_block0)]
+    for r in range(S.shape[0]):
+        I = q_block0 + r
         forced = set()
         if force_first:
             forced.add(0)
@@ -102,9 +109,9 @@ def select_blocks(S, mode, k=0, log_alpha=-np.log(20.0), force_first=False, forc
             forced.add(I)
         if mode == "topk":
             cand = [J for J in range(I + 1) if J not in forced]
-            sel = set(topk_rule(S[I], cand, k).tolist())
+            sel = set(topk_rule(S[r], cand, k).tolist())
         elif mode == "thresh":
-            sel = set(threshold_rule(S[I], np.arange(I + 1), log_alpha).tolist())
+            sel = set(threshold_rule(S[r], np.arange(I + 1), log_alpha).tolist())
         else:
             raise ValueError(mode)
         out.append(np.array(sorted(sel | forced), dtype=np.int64))

@@ -51,18 +51,22 @@ def assert_set_matches(gpu, scores, oracle_sel, cutoff, tol, expect_count=None, 
     assert not bad, f"{what}: {len(bad)} non-exempt differences, e.g. {sorted(bad)[:10]} (cutoff {cutoff})"
 
 
-def check_block_selection(gpu_idx, gpu_cnt, S, plan_mode, topk, log_alpha, ff, fd, what=""):
-    """Compare the GPU block lists of one head with the oracle rule on S."""
+def check_block_selection(gpu_idx, gpu_cnt, S, plan_mode, topk, log_alpha, ff, fd, what="", qb0=0):
+    """Compare the GPU block lists of one head with the oracle rule on S.
+
+    Row I of S and of the GPU lists is the chunk's query block I, absolute
+    block qb0 + I (qb0 = q_offset / block)."""
     nqb = S.shape[0]
     for I in range(nqb):
+        Ia = qb0 + I
         g = gpu_idx[I, :gpu_cnt[I]].tolist()
         forced = set()
         if ff:
             forced.add(0)
         if fd:
-            forced.add(I)
+            forced.add(Ia)
         if plan_mode == "topk":
-            cand = [J for J in range(I + 1) if J not in forced]
+            cand = [J for J in range(Ia + 1) if J not in forced]
             sel, c, tol = band_topk(S[I], cand, topk)
             expect = len(sel) + len(forced)
             g_rest = [j for j in g if j not in forced]
@@ -70,9 +74,9 @@ def check_block_selection(gpu_idx, gpu_cnt, S, plan_mode, topk, log_alpha, ff, f
             assert_set_matches(g_rest, S[I], sel, c, tol, expect_count=len(sel), what=f"{what} I={I}")
             assert len(g) == expect
         else:
-            row = S[I, :I + 1]
+            row = S[I, :Ia + 1]
             cut = row.max() + log_alpha
-            sel = set(O.threshold_rule(S[I], np.arange(I + 1), log_alpha).tolist())
+            sel = set(O.threshold_rule(S[I], np.arange(Ia + 1), log_alpha).tolist())
             tol = 1e-3 * max(1.0, abs(cut))
             assert forced <= set(g), f"{what} I={I}: forced blocks missing"
             assert_set_matches(g, S[I], sel | forced, cut, tol, what=f"{what} I={I}")
@@ -101,11 +105,13 @@ def oracle_head_sets(w, b, h):
         V, S = O.vs_select(v, s, p.nv, p.ns)
         return ("vs", V, S, v, s)
     if p.kind == dsa.BLOCK:
+        # a chunk's query blocks start at absolute block q_offset / block
+        qb0 = w.q_offset // p.block
         qb = O.block_means(f64(w.q[b, h]), p.block)
         kb = O.block_means(f64(w.k[b, kvh]), p.block)
-        S = O.block_scores(qb, kb)
+        S = O.block_scores(qb, kb, q_block0=qb0)
         sel = O.select_blocks(S, p.mode, k=p.topk, log_alpha=p.log_alpha, force_first=p.force_first,
-                              force_diag=p.force_diag)
+                              force_diag=p.force_diag, q_block0=qb0)
         return ("block", sel, S, qb, kb)
     return ("dense",)
 
@@ -137,7 +143,10 @@ def upload_sets(w, sets, device):
             dg[b, h, :len(S)] = torch.from_numpy(np.asarray(S, dtype=np.int32))
             dc[b, h] = len(S)
         elif s[0] == "block":
-            for I, lst in enumerate(s[1]):
+            # the oracle's lists are indexed by absolute query block; the
+            # device's by the chunk's query blocks
+            qb0 = w.q_offset // w.heads[h].block
+            for I, lst in enumerate(s[1][qb0:]):
                 bidx[b, h, I, :len(lst)] = torch.from_numpy(np.asarray(lst, dtype=np.int32))
                 bcnt[b, h, I] = len(lst)
     if vsi:

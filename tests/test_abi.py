@@ -138,7 +138,11 @@ def test_block_validation_paths():
     assert call(out=dsa._BlockIndexC(0x2000, 0x2000, 4, 128)) == dsa.DSA_ERR_INVALID_ARG
     assert call(out=dsa._BlockIndexC(0, 0x2000, 4, 64)) == dsa.DSA_ERR_INVALID_ARG
     assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
-    assert call(sh=shape(q_len=200, q_offset=56)) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(sh=shape(q_len=200, q_offset=56)) == dsa.DSA_ERR_UNSUPPORTED   # chunk not block-aligned
+    # a chunk at q_offset 128 (two query blocks, absolute 2 and 3): its last block
+    # has four candidates, so the threshold rule needs cap >= 4
+    assert call(sh=shape(q_len=128, q_offset=128), mode=1,
+                out=dsa._BlockIndexC(0x2000, 0x2000, 3, 64)) == dsa.DSA_ERR_INVALID_ARG
 
 
 def test_attention_validation_paths():
@@ -163,6 +167,7 @@ def test_attention_validation_paths():
     assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
     assert call(sh=shape(head_dim=96)) == dsa.DSA_ERR_UNSUPPORTED
     assert call(v=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG      # rows need 16-byte alignment
+    assert call(sh=shape(q_len=200, q_offset=56)) == dsa.DSA_ERR_UNSUPPORTED   # block heads: chunk not block-aligned
 
 
 def test_ashape_validation_paths():

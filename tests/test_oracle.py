@@ -163,6 +163,36 @@ def test_select_blocks_threshold_unforced():
         assert sel[I].tolist() == ref
 
 
+@pytest.mark.parametrize("mode", ["topk", "thresh"])
+def test_block_rule_chunk_equals_full_prompt_rows(mode):
+    # A prefill chunk whose first query sits at q_offset = q_block0 * block pools
+    # the same rows as the whole prompt's query blocks q_block0.., so its scores,
+    # selection, mask and attention equal the whole prompt's from there on.
+    rng = np.random.default_rng(21)
+    n, d, block, qb0 = 100, 16, 8, 5          # ragged last block
+    q, k, v = bf16_array((n, d), 2.0, rng), bf16_array((n, d), 2.0, rng), bf16_array((n, d), rng=rng)
+    off = qb0 * block
+    kb = O.block_means(k, block)
+    S_full = O.block_scores(O.block_means(q, block), kb)
+    S_chunk = O.block_scores(O.block_means(q[off:], block), kb, q_block0=qb0)
+    assert np.array_equal(S_chunk, S_full[qb0:])
+    kw = dict(k=3, log_alpha=-math.log(20), force_first=True, force_diag=True)
+    sel_full = O.select_blocks(S_full, mode, **kw)
+    sel_chunk = O.select_blocks(S_chunk, mode, q_block0=qb0, **kw)
+    assert len(sel_chunk) == len(sel_full)
+    for I in range(len(sel_full)):
+        assert sel_chunk[I].tolist() == (sel_full[I].tolist() if I >= qb0 else [])
+    m_full = O.mask_block(n, n, sel_full, block)
+    m_chunk = O.mask_block(n - off, n, sel_chunk, block, q_offset=off)
+    assert np.array_equal(m_chunk, m_full[off:])
+    o_f, l_f = O.masked_attention(q, k, v, m_full)
+    o_c, l_c = O.masked_attention(q[off:], k, v, m_chunk)
+    assert np.allclose(o_c, o_f[off:], atol=1e-13) and np.allclose(l_c, l_f[off:], atol=1e-13)
+    # the forced diagonal is the absolute block, and every list stays causal
+    for I in range(qb0, len(sel_chunk)):
+        assert I in sel_chunk[I] and sel_chunk[I].max() <= I
+
+
 # ---------------------------------------------------------------------------
 # Vertical-Slash rule
 # ---------------------------------------------------------------------------

@@ -169,6 +169,42 @@ def test_block_index_batch2(block, mode):
             check_block_selection(out.idx[b, h].cpu().numpy(), out.count[b, h].cpu().numpy(), S, mode, 4,
                                   -math.log(20.0), force, force, what=f"b{b} head {h}")
         assert int(out.count[b, 1].sum()) == 0, "unlisted head written"
+@pytest.mark.parametrize("N,off,block,mode,force", [(1500, 640, 64, "topk", True), (1500, 512, 128, "thresh", False),
+                                                    (1000, 608, 32, "thresh", True), (777, 400, 16, "topk", False),
+                                                    (2085, 1984, 64, "thresh", True)])
+def test_block_index_chunk(N, off, block, mode, force):
+    """build_index_block on a prefill chunk (q_offset > 0, a multiple of the
+    block; batch 2, GQA 3/1): the chunk's pooled queries bit-exact, the scores
+    of its query block I against key blocks J <= q_offset / block + I, and the
+    selections over those candidates, forced diagonal the absolute block."""
+    full = synth.block_planted(seed=60 + N, B=2, H=3, Hkv=1, N=N, block=block, n_plant=3, mode=mode, topk=4,
+                               force=force)
+    w = synth.Workload("block_chunk", full.q[:, :, off:].contiguous(), full.k, full.v, full.heads, q_offset=off)
+    q, k, _ = dev(w)
+    B, H, Hkv, Nq, Nk, d = w.shape
+    nqb, nkb, qb0 = -(-Nq // block), -(-Nk // block), off // block
+    cap = qb0 + nqb if mode == "thresh" else min(qb0 + nqb, 4 + 2 * force)
+    out = dsa.BlockIndex.empty(B, H, nqb, cap, block, DEV)
+    qbar = torch.zeros(B, H, nqb, 128, dtype=torch.bfloat16, device=DEV)
+    kbar = torch.zeros(B, Hkv, nkb, 128, dtype=torch.bfloat16, device=DEV)
+    scores = torch.zeros(B, H, nqb, nkb, dtype=torch.float32, device=DEV)
+    dsa.build_index_block(q, k, list(range(H)), block, dsa.TOPK if mode == "topk" else dsa.THRESHOLD, 4, out,
+                          force_first=force, force_diag=force, qbar=qbar, kbar=kbar, scores=scores)
+    torch.cuda.synchronize()
+    causal = np.arange(nkb)[None, :] <= np.arange(nqb)[:, None] + qb0
+    for b in range(B):
+        for h in range(H):
+            _, sel, S, qb, kb = oracle_head_sets(w, b, h)
+            assert S.shape == (nqb, nkb)
+            assert np.array_equal(f64(qbar[b, h].cpu()), qb), "pooled Q must be bit-exact"
+            assert np.array_equal(f64(kbar[b, 0].cpu()), kb), "pooled K must be bit-exact"
+            g = scores[b, h].cpu().double().numpy()
+            assert np.all(np.isneginf(g[~causal])) and np.all(np.isneginf(S[~causal]))
+            assert np.abs(g[causal] - S[causal]).max() <= 1e-5 * max(1.0, np.abs(S[causal]).max())
+            check_block_selection(out.idx[b, h].cpu().numpy(), out.count[b, h].cpu().numpy(), S, mode, 4,
+                                  -math.log(20.0), force, force, what=f"chunk b{b} head {h}", qb0=qb0)
+
+
 @pytest.mark.parametrize("N,last_q,nv,ns", [(1000, 64, 64, 64), (2048, 17, 100, 300), (130, 64, 8, 8)])
 def test_vs_index_parity(N, last_q, nv, ns):
     w = synth.vs_single(seed=30 + N, N=N, last_q=last_q, nv=nv, ns=ns, n_plant=4)

@@ -25,8 +25,8 @@ def vs(last_q, nv, ns):
     return synth.HeadPlan(dsa.VS, last_q=last_q, nv=nv, ns=ns)
 
 
-def blk(mode, topk=0, force=False):
-    return synth.HeadPlan(dsa.BLOCK, block=64, mode=mode, topk=topk, log_alpha=-float(np.log(20.0)),
+def blk(mode, topk=0, force=False, block=64):
+    return synth.HeadPlan(dsa.BLOCK, block=block, mode=mode, topk=topk, log_alpha=-float(np.log(20.0)),
                           force_first=force, force_diag=force)
 
 
@@ -172,3 +172,15 @@ def test_block_head_pairs(Nk):
     heads = [blk("topk", 5, True), blk("thresh"), blk("topk", 3), dense(),
              blk("thresh"), blk("topk", 7, True), vs(64, 20, 40), blk("topk", 2)]
     run_and_check(workload(80 + Nk, 2, 8, 2, Nk, heads), f"block pairs N={Nk}")
+
+
+@pytest.mark.parametrize("block", [16, 32, 64, 128])
+def test_block_heads_in_a_chunk(block):
+    """Block heads in a prefill chunk that starts at key 512 (a multiple of every
+    block size), with a ragged end: the lists are per query block of the chunk
+    and hold absolute key blocks.  Batch 2, GQA 8/2, top-k and threshold heads
+    beside Vertical-Slash and dense heads; for blocks of 64 the neighbouring
+    block heads of a KV group run as pairs."""
+    heads = [blk("topk", 3, True, block), blk("thresh", block=block), vs(64, 20, 40), dense(),
+             blk("thresh", block=block), blk("topk", 5, False, block), blk("topk", 2, True, block), ashape(16, 64)]
+    run_and_check(workload(140 + block, 2, 8, 2, 1300, heads, Nq=788), f"block {block} chunk")
