@@ -86,9 +86,10 @@ def lib() -> ctypes.CDLL:
         L.build_index_block.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, ctypes.c_float, I32, I32,
                                         _BlockIndexC, P, P, P, P, SZ, P]
         L.build_index_tokens.restype = I32
-        L.build_index_tokens.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, _TokenIndexC, P, P, SZ, P]
+        L.build_index_tokens.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, _TokenIndexC, P, P, SZ,
+                                         P]
         L.build_index_tokens_hier.restype = I32
-        L.build_index_tokens_hier.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, _TokenIndexC,
+        L.build_index_tokens_hier.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, I32, I32, I32, I32, _TokenIndexC,
                                               ctypes.POINTER(_TokenIndexC), P, P, SZ, P]
         L.sparse_prefill_attn.restype = I32
         L.sparse_prefill_attn.argtypes = [ctypes.POINTER(Shape), P, P, P, P, ctypes.POINTER(_VsIndexC),
@@ -255,34 +256,46 @@ def build_index_block(q, k, heads, block, mode, topk, out: BlockIndex, log_alpha
     return out
 
 
-def build_index_tokens(q_idx, k_idx, w, topk, out: TokenIndex, route_heads=0, route=None, ws=None):
+def _indexer_shape(q_idx, k_idx, w):
+    """Shape of an indexer call: q_idx [Nq, Hi, d] or [B, Nq, Hi, d], k_idx [Nk, d] or
+    [B, Nk, d], w [Nq, Hi] or [B, Nq, Hi] (the sequences of a batch run one after another)."""
+    if q_idx.dim() == 3:
+        Nq, Hi, di = q_idx.shape
+        B = 1
+    else:
+        B, Nq, Hi, di = q_idx.shape
+    Nk = k_idx.shape[-2]
+    if k_idx.numel() != B * Nk * di or w.numel() != B * Nq * Hi:
+        raise ValueError("q_idx, k_idx and w disagree on the batch or sizes")
+    return Shape(B, 1, 1, Nq, Nk, di, Nk - Nq), Hi
+
+
+def build_index_tokens(q_idx, k_idx, w, topk, out: TokenIndex, route_heads=0, route=None, ws=None, route_block=64):
     _need(q_idx, "q_idx", torch.bfloat16)
     _need(k_idx, "k_idx", torch.bfloat16, q_idx.device)
     _need(w, "w", torch.float32, q_idx.device)
-    Nq, Hi, di = q_idx.shape
-    Nk = k_idx.shape[0]
-    shape = Shape(1, 1, 1, Nq, Nk, di, Nk - Nq)
+    shape, Hi = _indexer_shape(q_idx, k_idx, w)
     ws = _workspace(OP_TOKENS, shape, [Hi, route_heads, topk], q_idx.device, ws)
-    _check(lib().build_index_tokens(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads, topk,
-                                    out.c(), _ptr(route), _ptr(ws), ws.numel(), _stream(q_idx.device)),
+    _check(lib().build_index_tokens(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads,
+                                    route_block, topk, out.c(), _ptr(route), _ptr(ws), ws.numel(),
+                                    _stream(q_idx.device)),
            "build_index_tokens")
     return out
 
 
 def build_index_tokens_hier(q_idx, k_idx, w, cand, topk, out: TokenIndex, route_heads=8, cands=None, route=None,
-                            ws=None):
+                            ws=None, route_block=64):
     """Hierarchical indexer: routed top-`cand` candidates, rescored by every head, top-`topk` of them."""
     _need(q_idx, "q_idx", torch.bfloat16)
     _need(k_idx, "k_idx", torch.bfloat16, q_idx.device)
     _need(w, "w", torch.float32, q_idx.device)
-    Nq, Hi, di = q_idx.shape
-    Nk = k_idx.shape[0]
-    shape = Shape(1, 1, 1, Nq, Nk, di, Nk - Nq)
+    shape, Hi = _indexer_shape(q_idx, k_idx, w)
     ws = _workspace(OP_TOKENS_HIER, shape, [Hi, route_heads, cand, topk], q_idx.device, ws)
     cc = cands.c() if cands is not None else None
-    _check(lib().build_index_tokens_hier(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads, cand,
-                                         topk, out.c(), ctypes.byref(cc) if cc is not None else None, _ptr(route),
-                                         _ptr(ws), ws.numel(), _stream(q_idx.device)),
+    _check(lib().build_index_tokens_hier(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w), Hi, route_heads,
+                                         route_block, cand, topk, out.c(),
+                                         ctypes.byref(cc) if cc is not None else None, _ptr(route), _ptr(ws),
+                                         ws.numel(), _stream(q_idx.device)),
            "build_index_tokens_hier")
     return out
 

@@ -115,6 +115,29 @@ size_t ws_vs_pooled(const dsa_shape* s, int n_heads, int block) {
 size_t ws_attn(const dsa_shape* s) { return align256(attn_workspace_bytes(s->batch, s->heads, s->kv_len)) + 256; }
 bool block_size_ok(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 
+// The indexer over a batch: one sequence after another on the caller's stream,
+// each with its slice of every per-sequence array; they share the workspace,
+// which stream order keeps from overlapping.
+hipError_t launch_indexer_batches(const IndexerArgs& a, int B, void* ws, hipStream_t st) {
+  for (int b = 0; b < B; ++b) {
+    IndexerArgs x = a;
+    const size_t rows = (size_t)b * a.Nq;
+    x.q_idx += rows * a.Hi * 128;
+    x.k_idx += (size_t)b * a.Nk * 128;
+    x.w += rows * a.Hi;
+    x.tok += rows * a.tok_cap;
+    x.tok_count += rows;
+    if (x.route) x.route += rows * a.route_heads;
+    if (x.cand_idx) {
+      x.cand_idx += rows * a.cand_cap;
+      x.cand_count += rows;
+    }
+    const hipError_t e = launch_indexer(x, ws, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,17 +386,18 @@ dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const vo
 }
 
 dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const void* k_idx, const float* w,
-                              int32_t n_idx_heads, int32_t route_heads, int32_t topk, dsa_token_index out,
-                              int32_t* route, void* ws, size_t ws_bytes, void* stream) {
+                              int32_t n_idx_heads, int32_t route_heads, int32_t route_block, int32_t topk,
+                              dsa_token_index out, int32_t* route, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   dsa_status st = check_shape(shape);
   if (st) return st;
   if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx or w is null");
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
-  if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 0 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
   if (route_heads > 8) return fail(DSA_ERR_UNSUPPORTED, "route_heads > 8");
+  if (route_heads > 0 && !block_size_ok(route_block))
+    return fail(DSA_ERR_UNSUPPORTED, "route_block %d (16, 32, 64 or 128)", route_block);
   // score rows are written through 32-bit buffer offsets (four rows per wave)
   if (shape->kv_len > (1 << 27)) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes kv_len <= 2^27");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
@@ -388,14 +412,15 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
   a.k_idx = (const uint16_t*)k_idx;
   a.w = w;
   a.Nq = shape->q_len; a.Nk = shape->kv_len; a.Hi = n_idx_heads; a.q_offset = shape->q_offset;
-  a.route_heads = route_heads; a.topk = topk;
+  a.route_heads = route_heads; a.topk = topk; a.route_block = route_heads > 0 ? route_block : 64;
   a.tok = out.idx; a.tok_count = out.count; a.tok_cap = out.cap;
   a.route = route;
-  return hip_status(launch_indexer(a, ws_base(ws), (hipStream_t)stream), "build_index_tokens");
+  return hip_status(launch_indexer_batches(a, shape->batch, ws_base(ws), (hipStream_t)stream), "build_index_tokens");
 }
 
 dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, const void* k_idx, const float* w,
-                                   int32_t n_idx_heads, int32_t route_heads, int32_t cand, int32_t topk,
+                                   int32_t n_idx_heads, int32_t route_heads, int32_t route_block, int32_t cand,
+                                   int32_t topk,
                                    dsa_token_index out, const dsa_token_index* cands, int32_t* route, void* ws,
                                    size_t ws_bytes, void* stream) {
   g_err.clear();
@@ -403,10 +428,10 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
   if (st) return st;
   if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx, k_idx or w is null");
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(DSA_ERR_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
-  if (shape->batch != 1) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes batch 1");
   if (n_idx_heads < 1 || n_idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "n_idx_heads must be in [1, 64]");
   if (route_heads < 1 || route_heads > n_idx_heads) return fail(DSA_ERR_INVALID_ARG, "route_heads out of range");
   if (route_heads > 8) return fail(DSA_ERR_UNSUPPORTED, "route_heads > 8");
+  if (!block_size_ok(route_block)) return fail(DSA_ERR_UNSUPPORTED, "route_block %d (16, 32, 64 or 128)", route_block);
   if (shape->kv_len > (1 << 27)) return fail(DSA_ERR_UNSUPPORTED, "the indexer takes kv_len <= 2^27");
   if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk < 1");
   if (topk > kMaxTokensPerQuery) return fail(DSA_ERR_UNSUPPORTED, "topk > %d", kMaxTokensPerQuery);
@@ -423,14 +448,15 @@ dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, co
   a.k_idx = (const uint16_t*)k_idx;
   a.w = w;
   a.Nq = shape->q_len; a.Nk = shape->kv_len; a.Hi = n_idx_heads; a.q_offset = shape->q_offset;
-  a.route_heads = route_heads; a.topk = topk;
+  a.route_heads = route_heads; a.topk = topk; a.route_block = route_block;
   a.tok = out.idx; a.tok_count = out.count; a.tok_cap = out.cap;
   a.route = route;
   a.cand = cand;
   a.cand_idx = cands ? cands->idx : nullptr;
   a.cand_count = cands ? cands->count : nullptr;
   a.cand_cap = cands ? cands->cap : cand;
-  return hip_status(launch_indexer(a, ws_base(ws), (hipStream_t)stream), "build_index_tokens_hier");
+  return hip_status(launch_indexer_batches(a, shape->batch, ws_base(ws), (hipStream_t)stream),
+                    "build_index_tokens_hier");
 }
 
 }  // extern "C"

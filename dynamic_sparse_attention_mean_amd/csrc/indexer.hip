@@ -711,7 +711,7 @@ IdxLayout idx_layout(int Nq, int Nk, int Hi, int R, int cand) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 0;
   L.off_scores = off; off = al(off + (size_t)Nq * Nk * 4);
-  L.off_kbar = off; off = al(off + (size_t)((Nk + 63) / 64) * 128 * 2);
+  L.off_kbar = off; off = al(off + (size_t)((Nk + 15) / 16) * 128 * 2);   // router blocks of 16 keys or more
   L.off_r = off; off = al(off + (size_t)Nq * Hi * 4);
   L.off_route = off; off = al(off + (size_t)Nq * std::max(R, 1) * 4);
   L.off_cand = off; off = al(off + (size_t)Nq * cand * 4);
@@ -736,7 +736,7 @@ hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
   q.q_idx = a.q_idx;
   q.w = a.w;
   q.Nq = a.Nq; q.Nk = a.Nk; q.Hi = a.Hi; q.q_offset = a.q_offset;
-  q.block = 64;
+  q.block = a.route_block;
   if (a.route_heads > 0) {
     // router: block means of the indexer keys, head scores, top-R heads
     uint16_t* kbar = (uint16_t*)(base + L.off_kbar);
@@ -745,10 +745,10 @@ hipError_t launch_indexer(const IndexerArgs& a, void* ws, hipStream_t st) {
     HeadList one;
     one.n = 1;
     one.h[0] = 0;
-    hipError_t e = launch_pool(a.k_idx, 1, 1, a.Nk, one, 64, kbar, st);
+    hipError_t e = launch_pool(a.k_idx, 1, 1, a.Nk, one, a.route_block, kbar, st);
     if (e != hipSuccess) return e;
     q.keys = kbar;
-    q.nkeys = (a.Nk + 63) / 64;
+    q.nkeys = (a.Nk + a.route_block - 1) / a.route_block;
     q.out = r;
     q.route = nullptr;
     q.R = 0;

@@ -139,6 +139,7 @@ struct IndexerArgs {
   const uint16_t* k_idx;   // [Nk, 128]
   const float* w;          // [Nq, Hi]
   int Nq, Nk, Hi, q_offset, route_heads, topk;
+  int route_block;         // keys per router block (16, 32, 64 or 128)
   int32_t* tok; int32_t* tok_count; int tok_cap;
   int32_t* route;          // nullable [Nq, route_heads]
   // hierarchical option (cand > 0): candidates per query, their list (nullable:

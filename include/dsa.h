@@ -217,15 +217,18 @@ dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const vo
  *   score[i, j] = sum_{h in H(i)} w[i, h] * max(0, q_idx[i, h] . k_idx[j]), j <= p_i
  *   route_heads == 0: H(i) = all heads.  route_heads = r > 0: H(i) = the r heads
  *   of largest w[i,h] * max(0, max_J q_idx[i,h] . Kbar_J), Kbar_J the bf16 mean of
- *   indexer keys [64J, 64J + 64) over complete blocks 64J + 63 <= p_i.
+ *   indexer keys [RJ, RJ + R) over complete blocks RJ + R - 1 <= p_i, R =
+ *   route_block in {16, 32, 64, 128} (read only when route_heads > 0).
  *   tokens = top-`topk` of score[i, :] (count min(topk, p_i + 1)).
- * q_idx: device bf16 [Nq, n_idx_heads, 128]; k_idx: device bf16 [Nk, 128]; w:
- * device float [Nq, n_idx_heads].  B must be 1.  route (nullable, device int32
- * [Nq, route_heads]) receives H(i) ascending.  out.cap >= topk.  Workspace:
+ * q_idx: device bf16 [B, Nq, n_idx_heads, 128]; k_idx: device bf16 [B, Nk, 128];
+ * w: device float [B, Nq, n_idx_heads]; out: [B, Nq, cap].  The sequences of a
+ * batch run one after another on `stream` and share the workspace.  route
+ * (nullable, device int32 [B, Nq, route_heads]) receives H(i) ascending.
+ * out.cap >= topk.  Workspace:
  * dsa_workspace_size(DSA_OP_TOKENS, {n_idx_heads, route_heads, topk}). */
 dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const void* k_idx,
                               const float* w, int32_t n_idx_heads, int32_t route_heads,
-                              int32_t topk, dsa_token_index out, int32_t* route,
+                              int32_t route_block, int32_t topk, dsa_token_index out, int32_t* route,
                               void* ws, size_t ws_bytes, void* stream);
 
 /* Hierarchical indexer token top-k ("MISA", section on how MISA works, the
@@ -238,12 +241,12 @@ dsa_status build_index_tokens(const dsa_shape* shape, const void* q_idx, const v
  *     . k_idx[j]) for j in C(i); tokens = top-`topk` of C(i) by it (ties to the
  *     lower index), ascending, min(topk, |C(i)|) keys.
  * Arguments as build_index_tokens, plus: route_heads in [1, 8]; topk <= 4096;
- * cand in [topk, 65536]; cands (nullable, device, cap >= cand) receives C(i)
+ * cand in [topk, 65536]; cands (nullable, device [B, Nq, cap], cap >= cand) receives C(i)
  * ascending, otherwise C(i) lives in the workspace.  Workspace:
  * dsa_workspace_size(DSA_OP_TOKENS_HIER, {n_idx_heads, route_heads, cand, topk}). */
 dsa_status build_index_tokens_hier(const dsa_shape* shape, const void* q_idx, const void* k_idx,
                                    const float* w, int32_t n_idx_heads, int32_t route_heads,
-                                   int32_t cand, int32_t topk, dsa_token_index out,
+                                   int32_t route_block, int32_t cand, int32_t topk, dsa_token_index out,
                                    const dsa_token_index* cands, int32_t* route,
                                    void* ws, size_t ws_bytes, void* stream);
 

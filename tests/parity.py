@@ -198,15 +198,16 @@ def assert_attention_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     return float(err.max()), float(err.mean())
 
 
-def check_hier_row(qf_i, kf, wf_i, p, route, cand, topk, kbar, g_route, g_cands, g_tok, what=""):
+def check_hier_row(qf_i, kf, wf_i, p, route, cand, topk, kbar, g_route, g_cands, g_tok, what="", rb=64):
     """One query of the hierarchical indexer against the oracle's own stages.
 
     The GPU's routing, candidates and final tokens are compared with the
     oracle's, each within its cutoff band; no GPU result feeds the oracle.
     Returns False when the GPU's routing or candidate choice fell inside a band
-    (the later stages then legitimately differ and are not compared)."""
+    (the later stages then legitimately differ and are not compared).  kbar:
+    the oracle's means of the indexer keys over router blocks of rb keys."""
     Hi = qf_i.shape[0]
-    nc = (p + 1) // 64
+    nc = (p + 1) // rb
     best = (kbar[:nc] @ qf_i.T).max(axis=0) if nc else np.zeros(Hi)
     r = wf_i * np.maximum(best, 0.0)
     sel, c, tol = band_topk(r, np.arange(Hi), route)

@@ -198,28 +198,30 @@ def test_tokens_validation_paths():
 
     def tok(**kw):
         return L.build_index_tokens(ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, FAKE, kw.get("hi", 64),
-                                    kw.get("r", 8), kw.get("topk", 100), kw.get("out", tok_c(100)), None,
-                                    kw.get("ws", FAKE), kw.get("wsb", need), None)
+                                    kw.get("r", 8), kw.get("rb", 64), kw.get("topk", 100), kw.get("out", tok_c(100)),
+                                    None, kw.get("ws", FAKE), kw.get("wsb", need), None)
 
     assert tok(hi=65) == dsa.DSA_ERR_UNSUPPORTED
-    assert L.build_index_tokens(ctypes.byref(sh), ctypes.c_void_p(0x1002), FAKE, FAKE, 64, 8, 100, tok_c(100), None,
-                                FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG   # q_idx not 16-byte aligned
+    assert L.build_index_tokens(ctypes.byref(sh), ctypes.c_void_p(0x1002), FAKE, FAKE, 64, 8, 64, 100, tok_c(100),
+                                None, FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG   # q_idx not 16-byte aligned
     assert tok(r=9) == dsa.DSA_ERR_UNSUPPORTED
+    assert tok(rb=48) == dsa.DSA_ERR_UNSUPPORTED and tok(rb=256) == dsa.DSA_ERR_UNSUPPORTED
     assert tok(topk=0) == dsa.DSA_ERR_INVALID_ARG
     assert tok(out=tok_c(50)) == dsa.DSA_ERR_INVALID_ARG
     assert tok(out=tok_c(100, null=True)) == dsa.DSA_ERR_INVALID_ARG
     assert tok(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
-    assert tok(sh=shape(batch=2, heads=1, kv_heads=1, q_len=64, kv_len=1024, q_offset=960)) == dsa.DSA_ERR_UNSUPPORTED
 
     def hier(**kw):
         c = kw.get("cands")
         return L.build_index_tokens_hier(ctypes.byref(sh), FAKE, FAKE, FAKE, kw.get("hi", 64), kw.get("r", 8),
-                                         kw.get("cand", 400), kw.get("topk", 100), kw.get("out", tok_c(100)),
+                                         kw.get("rb", 64), kw.get("cand", 400), kw.get("topk", 100),
+                                         kw.get("out", tok_c(100)),
                                          ctypes.byref(c) if c is not None else None, None, FAKE,
                                          kw.get("wsb", need_h), None)
 
     assert hier(r=0) == dsa.DSA_ERR_INVALID_ARG
     assert hier(r=9, hi=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert hier(rb=0) == dsa.DSA_ERR_UNSUPPORTED
     assert hier(cand=99) == dsa.DSA_ERR_INVALID_ARG
     assert hier(cand=65537, topk=100) == dsa.DSA_ERR_INVALID_ARG
     assert hier(topk=4097, cand=5000, out=tok_c(4097)) == dsa.DSA_ERR_UNSUPPORTED

@@ -18,6 +18,38 @@ def small_chunk(seed, N, Nq, Hi, topk, H=4):
     return synth.indexer_chunk(seed=seed, N=N, Nq=Nq, Hi=Hi, H=H, topk=topk)
 
 
+def check_token_rows(qi, ki, wt, idx, count, gr, N, Nq, topk, route, what="", rb=64):
+    """One sequence's token lists (and routing, when route > 0) against the
+    oracle outside the cutoff band; rows routed inside the band are skipped and
+    must be rare.  rb: keys per router block."""
+    qo = N - Nq
+    qf, kf, wf = f64(qi), f64(ki), wt.double().numpy()
+    heads = O.router_heads(qf, kf, wf, qo, route_heads=route, block=rb) if route else None
+    skipped = 0
+    if route:
+        # the GPU's routing decision, checked against the oracle router within the band
+        kbar = O.block_means(kf, rb)
+        for i in range(Nq):
+            p = i + qo
+            nc = (p + 1) // rb
+            best = (kbar[:nc] @ qf[i].T).max(axis=0) if nc else np.zeros(qf.shape[1])
+            r = wf[i] * np.maximum(best, 0.0)
+            sel, c, tol = band_topk(r, np.arange(qf.shape[1]), route)
+            assert_set_matches(gr[i], r, sel, c, tol, expect_count=route, what=f"{what} route q{i}")
+    for i in range(Nq):
+        p = i + qo
+        if route and set(gr[i].tolist()) != set(heads[i].tolist()):
+            skipped += 1            # a routing choice inside the band: the token scores differ by design
+            continue
+        sc = O.indexer_row(qf[i], kf, wf[i], p, None if heads is None else heads[i])
+        full = np.full(N, -np.inf)
+        full[:p + 1] = sc
+        sel, c, tol = band_topk(full, np.arange(p + 1), topk)
+        n = int(count[i])
+        assert_set_matches(idx[i, :n], full, sel, c, tol, expect_count=min(topk, p + 1), what=f"{what} tokens q{i}")
+    assert skipped <= max(2, Nq // 20), f"{what}: {skipped} of {Nq} queries routed inside the band"
+
+
 @pytest.mark.parametrize("N,Nq,Hi,topk,route", [(1000, 70, 64, 50, 0), (777, 33, 16, 700, 0),
                                                 (1500, 90, 64, 64, 8), (640, 64, 12, 100, 3)])
 def test_indexer_token_sets(N, Nq, Hi, topk, route):
@@ -28,34 +60,35 @@ def test_indexer_token_sets(N, Nq, Hi, topk, route):
     dsa.build_index_tokens(qi.to(DEV), ki.to(DEV), wt.to(DEV), topk, out, route_heads=route,
                            route=rt if route else None)
     torch.cuda.synchronize()
-    qo = N - Nq
-    qf, kf, wf = f64(qi), f64(ki), wt.double().numpy()
-    heads = O.router_heads(qf, kf, wf, qo, route_heads=route) if route else None
-    skipped = 0
-    if route:
-        # the GPU's routing decision, checked against the oracle router within the band
-        gr = rt.cpu().numpy()
-        kbar = O.block_means(kf, 64)
+    check_token_rows(qi, ki, wt, out.idx[0].cpu().numpy(), out.count[0].cpu().numpy(), rt.cpu().numpy(), N, Nq, topk,
+                     route)
+
+
+@pytest.mark.parametrize("route", [0, 8])
+def test_indexer_batch2(route):
+    """build_index_tokens over a batch of two chunks ([B, Nq, Hi, d] indexer
+    queries, [B, Nk, d] keys, [B, Nq, Hi] weights): every sequence against the
+    oracle, and equal to a call on that sequence alone."""
+    N, Nq, Hi, topk = 900, 48, 64, 80
+    ws = [small_chunk(31 + b, N, Nq, Hi, topk) for b in range(2)]
+    qi, ki, wt = (torch.stack([w.extra[x] for w in ws]) for x in ("q_idx", "k_idx", "w"))
+    out = dsa.TokenIndex.empty(2, Nq, topk, DEV)
+    rt = torch.full((2, Nq, max(route, 1)), -1, dtype=torch.int32, device=DEV)
+    dsa.build_index_tokens(qi.to(DEV), ki.to(DEV), wt.to(DEV), topk, out, route_heads=route,
+                           route=rt if route else None)
+    torch.cuda.synchronize()
+    for b in range(2):
+        check_token_rows(qi[b], ki[b], wt[b], out.idx[b].cpu().numpy(), out.count[b].cpu().numpy(),
+                         rt[b].cpu().numpy(), N, Nq, topk, route, what=f"b{b}")
+        one = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+        r1 = torch.full((Nq, max(route, 1)), -1, dtype=torch.int32, device=DEV)
+        dsa.build_index_tokens(qi[b].to(DEV), ki[b].to(DEV), wt[b].to(DEV), topk, one, route_heads=route,
+                               route=r1 if route else None)
+        torch.cuda.synchronize()
+        assert torch.equal(one.count[0], out.count[b]) and torch.equal(r1, rt[b])
         for i in range(Nq):
-            p = i + qo
-            nc = (p + 1) // 64
-            best = (kbar[:nc] @ qf[i].T).max(axis=0) if nc else np.zeros(Hi)
-            r = wf[i] * np.maximum(best, 0.0)
-            sel, c, tol = band_topk(r, np.arange(Hi), route)
-            assert_set_matches(gr[i], r, sel, c, tol, expect_count=route, what=f"route q{i}")
-    for i in range(Nq):
-        p = i + qo
-        if route and set(gr[i].tolist()) != set(heads[i].tolist()):
-            skipped += 1            # a routing choice inside the band: the token scores differ by design
-            continue
-        sc = O.indexer_row(qf[i], kf, wf[i], p, None if heads is None else heads[i])
-        full = np.full(N, -np.inf)
-        full[:p + 1] = sc
-        sel, c, tol = band_topk(full, np.arange(p + 1), topk)
-        n = int(out.count[0, i].item())
-        assert_set_matches(out.idx[0, i, :n].cpu().numpy(), full, sel, c, tol, expect_count=min(topk, p + 1),
-                           what=f"tokens q{i}")
-    assert skipped <= max(2, Nq // 20), f"{skipped} of {Nq} queries routed inside the band"
+            n = int(one.count[0, i])
+            assert torch.equal(one.idx[0, i, :n], out.idx[b, i, :n]), f"b{b} q{i}"
 
 
 @pytest.mark.parametrize("N,Nq,k", [(1000, 70, 50), (300, 300, 40), (513, 17, 600)])
@@ -163,6 +196,64 @@ def test_hierarchical_token_sets(N, Nq, Hi, route, cand, topk):
         c_o = O.token_topk(O.indexer_row(qf[i], kf, wf[i], p, h_o), p, cand)
         assert check_hier_row(qf[i], kf, wf[i], p, route, cand, topk, kbar, h_o, c_o, final[i], what=f"self q{i}")
     assert band_rows <= max(2, Nq // 20), f"{band_rows} of {Nq} rows chose inside a band"
+
+
+@pytest.mark.parametrize("rb", [16, 32, 128])
+def test_indexer_route_block(rb):
+    """Router blocks of 16, 32 and 128 keys (the route_block argument): the
+    routing and the token lists against the oracle router of that block size,
+    plain and hierarchical."""
+    N, Nq, Hi, topk, route, cand = 1100, 60, 64, 90, 8, 300
+    w = small_chunk(51 + rb, N, Nq, Hi, topk)
+    qi, ki, wt = w.extra["q_idx"], w.extra["k_idx"], w.extra["w"]
+    out = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+    rt = torch.full((Nq, route), -1, dtype=torch.int32, device=DEV)
+    dsa.build_index_tokens(qi.to(DEV), ki.to(DEV), wt.to(DEV), topk, out, route_heads=route, route=rt, route_block=rb)
+    torch.cuda.synchronize()
+    check_token_rows(qi, ki, wt, out.idx[0].cpu().numpy(), out.count[0].cpu().numpy(), rt.cpu().numpy(), N, Nq, topk,
+                     route, what=f"rb{rb}", rb=rb)
+    hout = dsa.TokenIndex.empty(1, Nq, topk, DEV)
+    cands = dsa.TokenIndex.empty(1, Nq, cand, DEV)
+    hrt = torch.full((Nq, route), -1, dtype=torch.int32, device=DEV)
+    dsa.build_index_tokens_hier(qi.to(DEV), ki.to(DEV), wt.to(DEV), cand, topk, hout, route_heads=route, cands=cands,
+                                route=hrt, route_block=rb)
+    torch.cuda.synchronize()
+    qf, kf, wf = f64(qi), f64(ki), wt.double().numpy()
+    kbar = O.block_means(kf, rb)
+    band_rows = 0
+    for i in range(Nq):
+        ok = check_hier_row(qf[i], kf, wf[i], i + N - Nq, route, cand, topk, kbar, hrt[i].cpu().numpy(),
+                            cands.idx[0, i, :cands.count[0, i]].cpu().numpy(),
+                            hout.idx[0, i, :hout.count[0, i]].cpu().numpy(), what=f"hier rb{rb} q{i}", rb=rb)
+        band_rows += not ok
+    assert band_rows <= max(2, Nq // 20), f"{band_rows} of {Nq} rows chose inside a band"
+
+
+def test_hierarchical_batch2():
+    """build_index_tokens_hier over a batch of two chunks, candidate lists
+    [B, Nq, cap] and routing [B, Nq, r]: every row of both sequences against the
+    oracle's own stages, as for one sequence."""
+    N, Nq, Hi, route, cand, topk = 800, 40, 64, 8, 256, 60
+    ws = [small_chunk(41 + b, N, Nq, Hi, topk) for b in range(2)]
+    qi, ki, wt = (torch.stack([w.extra[x] for w in ws]) for x in ("q_idx", "k_idx", "w"))
+    out = dsa.TokenIndex.empty(2, Nq, topk, DEV)
+    cands = dsa.TokenIndex.empty(2, Nq, cand, DEV)
+    rt = torch.full((2, Nq, route), -1, dtype=torch.int32, device=DEV)
+    dsa.build_index_tokens_hier(qi.to(DEV), ki.to(DEV), wt.to(DEV), cand, topk, out, route_heads=route, cands=cands,
+                                route=rt)
+    torch.cuda.synchronize()
+    qo = N - Nq
+    band_rows = 0
+    for b in range(2):
+        qf, kf, wf = f64(qi[b]), f64(ki[b]), wt[b].double().numpy()
+        kbar = O.block_means(kf, 64)
+        gr = rt[b].cpu().numpy()
+        for i in range(Nq):
+            ok = check_hier_row(qf[i], kf, wf[i], i + qo, route, cand, topk, kbar, gr[i],
+                                cands.idx[b, i, :cands.count[b, i]].cpu().numpy(),
+                                out.idx[b, i, :out.count[b, i]].cpu().numpy(), what=f"b{b} q{i}")
+            band_rows += not ok
+    assert band_rows <= max(2, Nq // 10), f"{band_rows} of {2 * Nq} rows chose inside a band"
 
 
 @pytest.mark.parametrize("H,Hkv,N,Nq,k,kinds", [
