@@ -108,7 +108,7 @@ size_t ws_vs_pooled(const dsa_shape* s, int n_heads, int block) {
   c.take<uint16_t>((size_t)s->batch * s->heads * nqb * 128);
   c.take<uint16_t>((size_t)s->batch * s->kv_heads * nkb * 128);
   c.take<float>((size_t)s->batch * n_heads * pooled_vs_partial_floats((int)nqb, (int)nkb));
-  c.take<float>((size_t)s->batch * n_heads * (nqb + nkb));
+  c.take<float>((size_t)s->batch * n_heads * (2 * nkb));
   return c.off + 256;
 }
 
@@ -335,7 +335,9 @@ dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const vo
   if (!q || !k) return fail(DSA_ERR_INVALID_ARG, "q or k is null");
   if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
   if (!block_size_ok(block)) return fail(DSA_ERR_UNSUPPORTED, "block %d (16, 32, 64 or 128)", block);
-  if (shape->q_offset != 0) return fail(DSA_ERR_UNSUPPORTED, "pooled discovery needs q_offset == 0");
+  if (shape->q_offset % block != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "pooled discovery needs q_offset (%d) to be a multiple of the block (%d)",
+                shape->q_offset, block);
   if (nv_blocks < 0 || ns_blocks < 0 || nv_blocks > kMaxPooledBlocks || ns_blocks > kMaxPooledBlocks)
     return fail(DSA_ERR_UNSUPPORTED, "nv_blocks and ns_blocks must be in [0, %d]", kMaxPooledBlocks);
   const int nqb = (shape->q_len + block - 1) / block, nkb = (shape->kv_len + block - 1) / block;
@@ -357,8 +359,8 @@ dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const vo
   uint16_t* kb = c.take<uint16_t>((size_t)shape->batch * shape->kv_heads * nkb * 128);
   const size_t pf = pooled_vs_partial_floats(nqb, nkb);
   float* part = c.take<float>(R * pf);
-  float* masses = c.take<float>(R * (nqb + nkb));
-  const int nstrips = (int)(pf / (size_t)(nqb + nkb));
+  float* masses = c.take<float>(R * (2 * nkb));
+  const int nstrips = (int)(pf / (size_t)(2 * nkb));
   float* vpart = part;
   float* spart = part + R * (size_t)nstrips * nkb;
   float* vbar = v_scores ? v_scores : masses;
@@ -378,7 +380,8 @@ dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const vo
   if ((st = hip_status(launch_pool((const uint16_t*)k, shape->batch, shape->kv_heads, shape->kv_len, kvl, block, kb, s),
                        "build_index_vs_pooled: pool k")))
     return st;
-  return hip_status(launch_pooled_vs(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb, shape->kv_len,
+  return hip_status(launch_pooled_vs(qb, kb, shape->batch, shape->heads, shape->kv_heads, nqb, nkb,
+                                     shape->q_offset / block, shape->kv_len,
                                      block, hl, (float)(1.0 / std::sqrt(128.0)), vpart, spart, vbar, sbar, nv_blocks,
                                      ns_blocks, out.cols, out.cols_count, out.cols_cap, out.diags, out.diags_count,
                                      out.diags_cap, s),

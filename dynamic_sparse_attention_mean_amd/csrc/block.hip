@@ -317,6 +317,10 @@ __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
 // a kept block (columns) and every token offset of a kept block offset
 // (diagonals D B - (B - 1) .. D B + (B - 1)).
 //
+// In a prefill chunk, query block I of the chunk is absolute block Ia = qb0 + I:
+// its softmax runs over J <= Ia and its slash terms are the offsets Ia - J, so
+// the slash masses have one entry per key block offset (nkb of them).
+//
 // pooled_vs_partial_kernel: a strip's scores on chip (strip_scores), each
 // row's softmax in place (wave r owns row r), then the strip's column sums and
 // block-diagonal sums, rows added in ascending order, to its slot of the
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(FB_THREADS) void block_index_kernel(
 // no term).  pooled_vs_combine_kernel adds the strips in ascending order:
 // vbar and sbar are bitwise reproducible.
 __global__ __launch_bounds__(FB_THREADS) void pooled_vs_partial_kernel(
-    const uint16_t* __restrict__ qbar, const uint16_t* __restrict__ kbar, int H, int Hkv, int nqb, int nkb,
+    const uint16_t* __restrict__ qbar, const uint16_t* __restrict__ kbar, int H, int Hkv, int nqb, int nkb, int qb0,
     HeadList heads, float scale, int R, int stride, int nstrips, float* __restrict__ vpart, float* __restrict__ spart) {
   __shared__ __align__(16) float s_sc[kBlockStripFloats];
   const int I0 = blockIdx.x * R;
@@ -333,13 +337,13 @@ __global__ __launch_bounds__(FB_THREADS) void pooled_vs_partial_kernel(
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int rows = min(R, nqb - I0);
-  const int nk = min(nkb, I0 + rows);
+  const int nk = min(nkb, qb0 + I0 + rows);
   strip_scores(qbar + ((size_t)(b * H + h) * nqb) * 128, kbar + ((size_t)(b * Hkv + kvh) * nkb) * 128, I0, rows,
                nk, scale, stride, s_sc);
   __syncthreads();
   if (w < rows) {
-    // P[I, J] = exp(S - max) / sum over J <= I; entries J > I become 0
-    const int I = I0 + w;
+    // P[I, J] = exp(S - max) / sum over J <= Ia; entries J > Ia become 0
+    const int I = qb0 + I0 + w;
     float* sr = s_sc + w * stride;
     constexpr float kLog2e = 1.4426950408889634f;
     float mx = -INFINITY;
@@ -359,20 +363,20 @@ __global__ __launch_bounds__(FB_THREADS) void pooled_vs_partial_kernel(
       for (int r = 0; r < rows; ++r) acc += s_sc[r * stride + J];
     vp[J] = acc;
   }
-  float* sp = spart + slot * nqb;
-  for (int D = tid; D < nqb; D += FB_THREADS) {
+  float* sp = spart + slot * nkb;
+  for (int D = tid; D < nkb; D += FB_THREADS) {
     float acc = 0.f;
     for (int r = 0; r < rows; ++r) {
-      const int J = I0 + r - D;
+      const int J = qb0 + I0 + r - D;
       if (J >= 0) acc += s_sc[r * stride + J];
     }
     sp[D] = acc;
   }
 }
 
-// vbar / sbar rows [B, n_heads, nkb] / [B, n_heads, nqb]: the strips' partials added in ascending order.
+// vbar / sbar rows [B, n_heads, nkb] each: the strips' partials added in ascending order.
 __global__ __launch_bounds__(256) void pooled_vs_combine_kernel(const float* __restrict__ vpart,
-                                                                const float* __restrict__ spart, int nqb, int nkb,
+                                                                const float* __restrict__ spart, int nkb,
                                                                 int n_heads, int nstrips, float* __restrict__ vbar,
                                                                 float* __restrict__ sbar) {
   const int x = blockIdx.x * 256 + threadIdx.x;
@@ -382,11 +386,11 @@ __global__ __launch_bounds__(256) void pooled_vs_combine_kernel(const float* __r
     float acc = 0.f;
     for (int t = 0; t < nstrips; ++t) acc += vpart[(row * nstrips + t) * nkb + x];
     vbar[row * nkb + x] = acc;
-  } else if (x < nkb + nqb) {
+  } else if (x < 2 * nkb) {
     const int D = x - nkb;
     float acc = 0.f;
-    for (int t = 0; t < nstrips; ++t) acc += spart[(row * nstrips + t) * nqb + D];
-    sbar[row * nqb + D] = acc;
+    for (int t = 0; t < nstrips; ++t) acc += spart[(row * nstrips + t) * nkb + D];
+    sbar[row * nkb + D] = acc;
   }
 }
 
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256) void pooled_vs_combine_kernel(const float* __r
 // sorts last), or the union of the kept offsets' diagonal ranges, ascending
 // (range i adds [max(lo_i, hi_(i-1) + 1), hi_i]: both ends ascend with D).
 __global__ __launch_bounds__(1024) void pooled_vs_select_kernel(const float* __restrict__ vbar,
-                                                                const float* __restrict__ sbar, int H, int nqb,
+                                                                const float* __restrict__ sbar, int H,
                                                                 int nkb, int Nk, int block, HeadList heads, int nvb,
                                                                 int nsb, int32_t* cols, int32_t* cols_count,
                                                                 int cols_cap, int32_t* diags, int32_t* diags_count,
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(1024) void pooled_vs_select_kernel(const float* __r
   const size_t bh = (size_t)b * H + h;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int m = which == 0 ? select_topk_3pass<1024>(vbar + row * nkb, nkb, nvb, s_sel, sm)
-                           : select_topk_3pass<1024>(sbar + row * nqb, nqb, nsb, s_sel, sm);
+                           : select_topk_3pass<1024>(sbar + row * nkb, nkb, nsb, s_sel, sm);
   __syncthreads();
   if (which == 0) {
     int32_t* out = cols + bh * cols_cap;
@@ -468,7 +472,7 @@ hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B,
 }
 
 hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
-                            int Nk, int block, const HeadList& heads, float scale, float* vpart, float* spart,
+                            int qb0, int Nk, int block, const HeadList& heads, float scale, float* vpart, float* spart,
                             float* vbar, float* sbar, int nvb, int nsb, int32_t* cols, int32_t* cols_count,
                             int cols_cap, int32_t* diags, int32_t* diags_count, int diags_cap, hipStream_t st) {
   if (heads.n == 0) return hipSuccess;
@@ -477,10 +481,10 @@ hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, i
   if (R < 1 || nvb > kMaxPooledBlocks || nsb > kMaxPooledBlocks) return hipErrorInvalidValue;
   const int nstrips = (nqb + R - 1) / R;
   hipLaunchKernelGGL(pooled_vs_partial_kernel, dim3(nstrips, heads.n, B), dim3(FB_THREADS), 0, st, qbar, kbar, H, Hkv,
-                     nqb, nkb, heads, scale, R, stride, nstrips, vpart, spart);
-  hipLaunchKernelGGL(pooled_vs_combine_kernel, dim3((nkb + nqb + 255) / 256, heads.n, B), dim3(256), 0, st, vpart,
-                     spart, nqb, nkb, heads.n, nstrips, vbar, sbar);
-  hipLaunchKernelGGL(pooled_vs_select_kernel, dim3(2, heads.n, B), dim3(1024), 0, st, vbar, sbar, H, nqb, nkb, Nk, block,
+                     nqb, nkb, qb0, heads, scale, R, stride, nstrips, vpart, spart);
+  hipLaunchKernelGGL(pooled_vs_combine_kernel, dim3((2 * nkb + 255) / 256, heads.n, B), dim3(256), 0, st, vpart,
+                     spart, nkb, heads.n, nstrips, vbar, sbar);
+  hipLaunchKernelGGL(pooled_vs_select_kernel, dim3(2, heads.n, B), dim3(1024), 0, st, vbar, sbar, H, nkb, Nk, block,
                      heads, nvb, nsb, cols, cols_count, cols_cap, diags, diags_count, diags_cap);
   return hipGetLastError();
 }
@@ -488,7 +492,7 @@ hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, i
 size_t pooled_vs_partial_floats(int nqb, int nkb) {
   const int R = block_strip_rows(nkb, nullptr);
   const size_t nstrips = R >= 1 ? (size_t)(nqb + R - 1) / R : 0;
-  return nstrips * (size_t)(nqb + nkb);
+  return nstrips * (size_t)(2 * nkb);
 }
 
 hipError_t launch_pool(const uint16_t* src, int B, int Hs, int N, const HeadList& heads, int block, uint16_t* dst,

@@ -45,14 +45,15 @@ hipError_t launch_block_index(const uint16_t* qbar, const uint16_t* kbar, int B,
                               float* scores, hipStream_t st);
 
 // Vertical and slash discovery from the pooled block scores: per listed head,
-// the per-strip partials (vpart [B, n_heads, nstrips, nkb], spart [.., nqb];
+// the per-strip partials (vpart [B, n_heads, nstrips, nkb], spart [.., nkb];
 // pooled_vs_partial_floats() per row of B * n_heads), the masses vbar
-// [B, n_heads, nkb] and sbar [B, n_heads, nqb], the top nvb key blocks and nsb
-// block offsets, expanded into the Vertical-Slash set ([B, H, cap] rows).
+// [B, n_heads, nkb] and sbar [B, n_heads, nkb] (one per key block offset), the
+// top nvb key blocks and nsb block offsets, expanded into the Vertical-Slash
+// set ([B, H, cap] rows).  Query block I of a chunk is absolute block qb0 + I.
 constexpr int kMaxPooledBlocks = 1024;     // kept key blocks / block offsets per head
 size_t pooled_vs_partial_floats(int nqb, int nkb);
 hipError_t launch_pooled_vs(const uint16_t* qbar, const uint16_t* kbar, int B, int H, int Hkv, int nqb, int nkb,
-                            int Nk, int block, const HeadList& heads, float scale, float* vpart, float* spart,
+                            int qb0, int Nk, int block, const HeadList& heads, float scale, float* vpart, float* spart,
                             float* vbar, float* sbar, int nvb, int nsb, int32_t* cols, int32_t* cols_count,
                             int cols_cap, int32_t* diags, int32_t* diags_count, int diags_cap, hipStream_t st);
 

@@ -190,19 +190,20 @@ dsa_status build_index_block(const dsa_shape* shape, const void* q, const void* 
  * section 2.1: one search over blocks, keys represented by their block means,
  * finds the vertical, slash and block shapes at once; the page states no rule
  * for the first two, this is the one the library defines).  For each listed head:
- *   Qbar, Kbar, S[I, J] = Qbar_I . Kbar_J / sqrt(d) (J <= I) as in
- *   build_index_block; P[I, :] = softmax over J <= I of S[I, J];
+ *   Qbar, Kbar, S[I, J] = Qbar_I . Kbar_J / sqrt(d) (J <= Ia) as in
+ *   build_index_block (query block I of the chunk is absolute block Ia =
+ *   q_offset / block + I); P[I, :] = softmax over J <= Ia of S[I, J];
  *   vbar[J] = sum_I P[I, J] (vertical mass of key block J),
- *   sbar[D] = sum_I P[I, I - D] (slash mass of block offset D);
+ *   sbar[D] = sum_I P[I, Ia - D] (slash mass of block offset D, D < nkb);
  *   kept key blocks = top-nv_blocks of vbar, kept offsets = top-ns_blocks of
  *   sbar (ties to the lower index);
  *   cols = every key of a kept key block, diags = every token offset
  *   [max(0, D*block - (block-1)), min(Nk-1, D*block + (block-1))] of a kept D.
  * The result goes to `out` like build_index_vs (attention takes it as a
- * Vertical-Slash set).  block in {16, 32, 64, 128}; q_offset must be 0;
+ * Vertical-Slash set).  block in {16, 32, 64, 128}; q_offset a multiple of block;
  * 0 <= nv_blocks, ns_blocks <= 1024; cols_cap >= min(Nk, nv_blocks * block),
  * diags_cap >= min(Nk, ns_blocks * (2 * block - 1)); at most 32768 key blocks.
- * v_scores ([B, n_heads, nkb]) and s_scores ([B, n_heads, nqb]), nullable
+ * v_scores ([B, n_heads, nkb]) and s_scores ([B, n_heads, nkb]), nullable
  * device floats, receive vbar and sbar in listed order.  Workspace:
  * dsa_workspace_size(DSA_OP_VS_POOLED, {n_heads, block}). */
 dsa_status build_index_vs_pooled(const dsa_shape* shape, const void* q, const void* k,

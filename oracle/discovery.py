@@ -35,15 +35,20 @@ import numpy as np
 from .rules import topk_rule
 
 
-def pooled_vs_scores(S):
-    """vbar [nkb] and sbar [nqb] from a block score matrix S (-inf above the
-    diagonal): the column and block-diagonal sums of the row-softmax of S."""
+def pooled_vs_scores(S, q_block0=0):
+    """vbar [nkb] and sbar [nkb] from a block score matrix S (-inf beyond the
+    causal bound): the column and block-diagonal sums of the row-softmax of S.
+
+    Row r of S is absolute query block I = q_block0 + r (block_scores of a
+    prefill chunk): its softmax runs over J <= I and its slash terms are the
+    offsets D = I - J, so sbar has one entry per key block offset."""
     S = np.asarray(S, dtype=np.float64)
     nq, nk = S.shape
     vbar = np.zeros(nk)
-    sbar = np.zeros(nq)
-    for I in range(nq):
-        row = S[I, :I + 1]
+    sbar = np.zeros(nk)
+    for r in range(nq):
+        I = q_block0 + r
+        row = S[r, :I + 1]
         e = np.exp(row - row.max())
         p = e / e.sum()
         vbar[:I + 1] += p
@@ -71,12 +76,15 @@ def expand_blocks(Vb, Sb, block, nk):
     return np.flatnonzero(cols).astype(np.int64), np.flatnonzero(diags).astype(np.int64)
 
 
-def pooled_vs_sets(q, k, block, nv_blocks, ns_blocks):
-    """The whole rule for one head: q [N, d], k [N, d] (bf16 values in float64,
-    a prefill that starts at key 0).  Returns (cols, diags, vbar, sbar, Vb, Sb)."""
+def pooled_vs_sets(q, k, block, nv_blocks, ns_blocks, q_offset=0):
+    """The whole rule for one head: q [Nq, d], k [Nk, d] (bf16 values in
+    float64; a prefill chunk whose first query sits at q_offset, a multiple of
+    the block, Nq = Nk - q_offset).  Returns (cols, diags, vbar, sbar, Vb, Sb)."""
     from .rules import block_means, block_scores
-    S = block_scores(block_means(q, block), block_means(k, block))
-    vbar, sbar = pooled_vs_scores(S)
+    assert q_offset % block == 0
+    qb0 = q_offset // block
+    S = block_scores(block_means(q, block), block_means(k, block), q_block0=qb0)
+    vbar, sbar = pooled_vs_scores(S, q_block0=qb0)
     Vb, Sb = pooled_vs_blocks(vbar, sbar, nv_blocks, ns_blocks)
     cols, diags = expand_blocks(Vb, Sb, block, np.asarray(k).shape[0])
     return cols, diags, vbar, sbar, Vb, Sb

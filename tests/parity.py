@@ -96,7 +96,7 @@ def oracle_head_sets(w, b, h):
         return ("vs", V, S, None, None)
     if p.kind == dsa.VS and getattr(p, "pooled", False):
         cols, diags, vbar, sbar, Vb, Sb = O.pooled_vs_sets(f64(w.q[b, h]), f64(w.k[b, kvh]), p.block, p.nv_blocks,
-                                                           p.ns_blocks)
+                                                           p.ns_blocks, q_offset=w.q_offset)
         return ("vs", cols, diags, vbar, sbar)
     if p.kind == dsa.VS:
         q = f64(w.q[b, h, Nq - p.last_q:])

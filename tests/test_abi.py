@@ -117,6 +117,28 @@ def test_vs_validation_paths():
     assert b"workspace" in L.dsa_last_error() or True
 
 
+def test_vs_pooled_validation_paths():
+    L = dsa.lib()
+    heads = (ctypes.c_int32 * 1)(1)
+    sh = shape()
+    _, need = ws_size(dsa.OP_VS_POOLED, sh, [1, 64])
+
+    def call(**kw):
+        return L.build_index_vs_pooled(ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, heads, 1, kw.get("block", 64),
+                                       kw.get("nv", 2), kw.get("ns", 2), kw.get("out", vs_c(128, 254)), None, None,
+                                       kw.get("ws", FAKE), kw.get("wsb", need), None)
+    assert call(block=48) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(nv=1025) == dsa.DSA_ERR_UNSUPPORTED and call(ns=-1) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(out=vs_c(127, 254)) == dsa.DSA_ERR_INVALID_ARG      # two key blocks of 64 need 128 columns
+    assert call(out=vs_c(128, 253)) == dsa.DSA_ERR_INVALID_ARG      # two offsets need 2 * 127 diagonals
+    assert call(out=vs_c(128, 254, null=True)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(sh=shape(q_len=200, q_offset=56)) == dsa.DSA_ERR_UNSUPPORTED   # chunk not block-aligned
+    # a chunk adds no workspace beyond the whole prompt's (the slash masses have one entry per key block)
+    st, need_c = ws_size(dsa.OP_VS_POOLED, shape(q_len=128, q_offset=128), [1, 64])
+    assert st == 0 and need_c <= need
+
+
 def test_block_validation_paths():
     L = dsa.lib()
     heads = (ctypes.c_int32 * 1)(0)

@@ -505,16 +505,18 @@ def test_hierarchical_special_cases():
 # ---------------------------------------------------------------------------
 # Vertical and slash discovery from pooled block scores (reading O-22)
 # ---------------------------------------------------------------------------
-def _pooled_brute(S):
-    """Row softmax and its column / block-diagonal sums with explicit loops."""
+def _pooled_brute(S, qb0=0):
+    """Row softmax and its column / block-diagonal sums with explicit loops;
+    row r is absolute query block qb0 + r."""
     nq, nk = S.shape
     v = [0.0] * nk
-    s = [0.0] * nq
-    for I in range(nq):
-        m = max(S[I][J] for J in range(I + 1))
-        den = sum(math.exp(S[I][J] - m) for J in range(I + 1))
+    s = [0.0] * nk
+    for r in range(nq):
+        I = qb0 + r
+        m = max(S[r][J] for J in range(I + 1))
+        den = sum(math.exp(S[r][J] - m) for J in range(I + 1))
         for J in range(I + 1):
-            p = math.exp(S[I][J] - m) / den
+            p = math.exp(S[r][J] - m) / den
             v[J] += p
             s[I - J] += p
     return np.array(v), np.array(s)
@@ -530,6 +532,25 @@ def test_pooled_vs_scores_brute_force(nq):
     # every row's weights sum to one: both masses total the number of query blocks
     assert abs(v.sum() - nq) < 1e-12 and abs(s.sum() - nq) < 1e-12
     assert np.all(v >= 0) and np.all(s >= 0) and v.max() <= nq and s.max() <= nq
+
+
+@pytest.mark.parametrize("qb0", [1, 5, 16])
+def test_pooled_vs_scores_chunk_adds_up_to_whole_prompt(qb0):
+    """Each query block adds its own softmax at its absolute block, so the
+    masses of a prefill chunk (query blocks qb0..) plus those of the earlier
+    query blocks are the whole prompt's; the chunk alone also matches the loops
+    at absolute positions."""
+    n = 17
+    S = RNG.standard_normal((n, n)) * 3.0
+    S = np.where(np.tril(np.ones((n, n), dtype=bool)), S, -np.inf)
+    v, s = O.pooled_vs_scores(S)
+    v1, s1 = O.pooled_vs_scores(S[:qb0])
+    v2, s2 = O.pooled_vs_scores(S[qb0:], q_block0=qb0)
+    assert len(s1) == len(s2) == n
+    assert np.allclose(v1 + v2, v, rtol=1e-12, atol=1e-14) and np.allclose(s1 + s2, s, rtol=1e-12, atol=1e-14)
+    vb, sb = _pooled_brute(S[qb0:], qb0)
+    assert np.allclose(v2, vb, rtol=1e-12, atol=1e-14) and np.allclose(s2, sb, rtol=1e-12, atol=1e-14)
+    assert abs(v2.sum() - (n - qb0)) < 1e-12 and abs(s2.sum() - (n - qb0)) < 1e-12
 
 
 def test_pooled_vs_scores_equal_scores_harmonic():

@@ -259,6 +259,38 @@ def test_vs_pooled_parity(B, H, Hkv, N, block, nvb, nsb, heads):
                               nsb, N, what=f"b{b} h{h}")
 
 
+@pytest.mark.parametrize("B,H,Hkv,N,off,block,nvb,nsb,heads", [(1, 2, 1, 1500, 640, 64, 3, 4, [0, 1]),
+                                                            (2, 4, 2, 2085, 1024, 32, 8, 10, [3, 0, 2]),
+                                                            (1, 1, 1, 1000, 896, 128, 2, 5, [0])])
+def test_vs_pooled_chunk(B, H, Hkv, N, off, block, nvb, nsb, heads):
+    """Pooled discovery in a prefill chunk (q_offset a multiple of the block):
+    query block I of the chunk is absolute block q_offset / block + I, so the
+    slash masses have one entry per key block offset; masses, kept blocks and
+    offsets, and the token sets against the oracle's."""
+    full = synth.vs_multi(seed=90 + N + block, B=B, H=H, Hkv=Hkv, Nk=N, n_plant=6)
+    w = synth.Workload("pooled_chunk", full.q[:, :, off:].contiguous(), full.k, full.v, full.heads, q_offset=off)
+    q, k, _ = dev(w)
+    nqb, nkb = -(-(N - off) // block), -(-N // block)
+    out = dsa.VSIndex.empty(B, H, min(N, nvb * block), min(N, nsb * (2 * block - 1)), DEV)
+    vsc = torch.zeros(B, len(heads), nkb, device=DEV)
+    ssc = torch.zeros(B, len(heads), nkb, device=DEV)
+    dsa.build_index_vs_pooled(q, k, heads, block, nvb, nsb, out, v_scores=vsc, s_scores=ssc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for t, h in enumerate(heads):
+            cols, diags, vbar, sbar, Vb, Sb = O.pooled_vs_sets(f64(w.q[b, h]), f64(w.k[b, h // (H // Hkv)]), block,
+                                                               nvb, nsb, q_offset=off)
+            assert len(vbar) == len(sbar) == nkb
+            for name, got, ref in (("vbar", vsc[b, t], vbar), ("sbar", ssc[b, t], sbar)):
+                g = got.cpu().double().numpy()
+                tol = 1e-5 * np.abs(ref) + 1e-7 * ref.sum() / len(ref)
+                assert np.all(np.abs(g - ref) <= tol), f"b{b} h{h} {name}: {np.abs(g - ref).max():.3g}"
+            assert abs(vsc[b, t].sum().item() - nqb) < 1e-3 * nqb and abs(ssc[b, t].sum().item() - nqb) < 1e-3 * nqb
+            check_pooled_sets(out.cols[b, h, :int(out.cols_count[b, h])].cpu().numpy(),
+                              out.diags[b, h, :int(out.diags_count[b, h])].cpu().numpy(), vbar, sbar, block, nvb,
+                              nsb, N, what=f"chunk b{b} h{h}")
+
+
 def test_ashape_sets():
     w = synth.random_qkv(1, 1, 3, 1, 500)
     q, k, v = (t.to(DEV) for t in w)
