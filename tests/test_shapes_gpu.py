@@ -184,3 +184,13 @@ def test_block_heads_in_a_chunk(block):
     heads = [blk("topk", 3, True, block), blk("thresh", block=block), vs(64, 20, 40), dense(),
              blk("thresh", block=block), blk("topk", 5, False, block), blk("topk", 2, True, block), ashape(16, 64)]
     run_and_check(workload(140 + block, 2, 8, 2, 1300, heads, Nq=788), f"block {block} chunk")
+
+
+@pytest.mark.parametrize("Nk,Nq,block", [(1025, 1, 64), (1041, 17, 16), (640, 128, 128), (2049, 1, 32)])
+def test_small_chunks_at_the_end(Nk, Nq, block):
+    """Chunks of one to a few queries at the end of the keys (q_offset a
+    multiple of the block): block heads of both rules beside Vertical-Slash,
+    A-shape and dense heads, batch 2."""
+    heads = [blk("topk", 3, True, block), blk("thresh", block=block), vs(min(Nq, 64), 20, 40), dense(),
+             ashape(16, 64), blk("topk", 1, False, block), vs(min(Nq, 64), 0, 30), blk("thresh", block=block)]
+    run_and_check(workload(170 + Nk + Nq, 2, 8, 2, Nk, heads, Nq=Nq), f"chunk Nk={Nk} Nq={Nq} block {block}")
