@@ -90,7 +90,8 @@ def check_vs_sets(out, b, h, v, s, nv, ns, what):
 
 @pytest.mark.parametrize("B,H,Hkv,Nk,Nq,heads,last_q", [(2, 4, 2, 1000, 1000, [3, 0, 2], 64),
                                                         (1, 4, 2, 1280, 320, [1, 2, 3], 64),
-                                                        (2, 2, 1, 900, 333, [1, 0], 33)])
+                                                        (2, 2, 1, 900, 333, [1, 0], 33),
+                                                        (1, 2, 1, 700, 1, [0, 1], 1)])
 def test_vs_index_batch_and_chunk(B, H, Hkv, Nk, Nq, heads, last_q):
     """build_index_vs with batch 2, heads listed out of order, and chunks that
     end at the last key (q_offset = Nk - Nq > 0): the v / s rows (listed order)
@@ -171,7 +172,8 @@ def test_block_index_batch2(block, mode):
         assert int(out.count[b, 1].sum()) == 0, "unlisted head written"
 @pytest.mark.parametrize("N,off,block,mode,force", [(1500, 640, 64, "topk", True), (1500, 512, 128, "thresh", False),
                                                     (1000, 608, 32, "thresh", True), (777, 400, 16, "topk", False),
-                                                    (2085, 1984, 64, "thresh", True)])
+                                                    (2085, 1984, 64, "thresh", True), (1025, 1024, 64, "topk", True),
+                                                    (2049, 2048, 128, "thresh", False)])
 def test_block_index_chunk(N, off, block, mode, force):
     """build_index_block on a prefill chunk (q_offset > 0, a multiple of the
     block; batch 2, GQA 3/1): the chunk's pooled queries bit-exact, the scores
@@ -261,7 +263,8 @@ def test_vs_pooled_parity(B, H, Hkv, N, block, nvb, nsb, heads):
 
 @pytest.mark.parametrize("B,H,Hkv,N,off,block,nvb,nsb,heads", [(1, 2, 1, 1500, 640, 64, 3, 4, [0, 1]),
                                                             (2, 4, 2, 2085, 1024, 32, 8, 10, [3, 0, 2]),
-                                                            (1, 1, 1, 1000, 896, 128, 2, 5, [0])])
+                                                            (1, 1, 1, 1000, 896, 128, 2, 5, [0]),
+                                                            (1, 2, 1, 1025, 1024, 64, 4, 4, [1])])
 def test_vs_pooled_chunk(B, H, Hkv, N, off, block, nvb, nsb, heads):
     """Pooled discovery in a prefill chunk (q_offset a multiple of the block):
     query block I of the chunk is absolute block q_offset / block + I, so the
