@@ -451,6 +451,60 @@ def test_router_brute_force():
         assert route[i].tolist() == ref
 
 
+def test_router_invariances():
+    """Properties any implementation of the router reading keeps, each failing
+    under a plausible slip: a per-row positive scale of w (ranking by w plus a
+    score), a block replaced by copies of its bf16 mean (raw keys instead of
+    block means), keys after the last complete block (partial blocks counted),
+    and scores all below zero (no ReLU: the heads would not tie at 0)."""
+    rng = np.random.default_rng(21)
+    nq, nk, Hi, di, blk, qo, rh = 5, 61, 7, 16, 8, 50, 3
+    q = bf16_array((nq, Hi, di), rng=rng)
+    k = bf16_array((nk, di), rng=rng)
+    w = rng.random((nq, Hi))
+    base = O.router_heads(q, k, w, qo, route_heads=rh, block=blk)
+    c = rng.uniform(0.1, 10.0, size=(nq, 1))
+    assert np.array_equal(O.router_heads(q, k, w * c, qo, route_heads=rh, block=blk), base)
+    k2 = k.copy()
+    for J in range(nk // blk):
+        k2[J * blk:(J + 1) * blk] = O.round_bf16(k[J * blk:(J + 1) * blk].sum(0) / blk)
+    assert np.array_equal(O.router_heads(q, k2, w, qo, route_heads=rh, block=blk), base)
+    # rows i see positions p = i + qo; the complete blocks end at 8 * ((p + 1) // 8)
+    k3 = k.copy()
+    pmin = qo
+    k3[8 * ((pmin + 1) // 8):] = 100.0
+    i0 = [i for i in range(nq) if (i + qo + 1) // blk == (pmin + 1) // blk]
+    got = O.router_heads(q, k3, w, qo, route_heads=rh, block=blk)
+    assert np.array_equal(got[i0], base[i0])
+    qn = -np.abs(q)
+    kp = np.abs(k)
+    assert np.array_equal(O.router_heads(qn, kp, w, qo, route_heads=rh, block=blk),
+                          np.tile(np.arange(rh), (nq, 1)))
+
+
+def test_select_blocks_threshold_forced_is_union():
+    """Under the threshold rule the forced blocks join the unforced set and the
+    row maximum stays the one over every causal candidate (a maximum taken
+    without the forced blocks would move the cutoff); with alpha -> 0 every
+    causal block is kept."""
+    rng = np.random.default_rng(9)
+    S = O.block_scores(bf16_array((9, 8), 4.0, rng), bf16_array((9, 8), 4.0, rng))
+    free = O.select_blocks(S, "thresh", log_alpha=-math.log(20))
+    forced = O.select_blocks(S, "thresh", log_alpha=-math.log(20), force_first=True, force_diag=True)
+    for I in range(9):
+        assert forced[I].tolist() == sorted(set(free[I].tolist()) | {0, I})
+    # a diagonal block far above the rest: the cutoff follows it, forced or not
+    S2 = S.copy()
+    for I in range(9):
+        S2[I, I] = S[I, :I + 1].max() + 10.0
+    f2 = O.select_blocks(S2, "thresh", log_alpha=-math.log(20), force_diag=True)
+    for I in range(9):
+        assert f2[I].tolist() == [I]
+    allk = O.select_blocks(S, "thresh", log_alpha=-1e9, force_first=True)
+    for I in range(9):
+        assert allk[I].tolist() == list(range(I + 1))
+
+
 def test_hierarchical_brute_force():
     """Both stages written out with plain loops and sorts on a tiny chunk."""
     nq, nk, Hi, di, blk, qo = 4, 48, 6, 8, 8, 40
