@@ -172,26 +172,15 @@ __device__ __forceinline__ void strip_scores(const uint16_t* __restrict__ qp, co
     qf[kk] = __builtin_bit_cast(bf16x8, x);
   }
   const int ntile = (nk + 15) / 16;
-  // A operand of tile t: this lane's key 16 t + l % 16, clamped into [0, nk)
-  // (entries of keys >= nk are never read as scores), loaded one tile ahead so
-  // that a tile's four loads are in flight together and overlap the products
-  // of the tile before.
-  auto load_tile = [&](int t, u32x4 (&x)[4]) {
-    const int key = min(16 * t + (l & 15), nk - 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) x[kk] = *(const u32x4*)(kp + (size_t)key * 128 + 32 * kk + 8 * kg);
-  };
-  u32x4 xn[4];
-  if (w < ntile) load_tile(w, xn);
   for (int t = w; t < ntile; t += FB_WAVES) {
-    u32x4 x[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) x[kk] = xn[kk];
-    if (t + FB_WAVES < ntile) load_tile(t + FB_WAVES, xn);
+    const int key = 16 * t + (l & 15);               // A operand row: this lane's key
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[kk]), qf[kk], acc, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < nk) x = *(const u32x4*)(kp + (size_t)key * 128 + 32 * kk + 8 * kg);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), qf[kk], acc, 0, 0, 0);
+    }
     // acc[i] = S[row qr][key 16 t + 4 kg + i]
     if (qr < rows) *(f32x4*)&s_sc[qr * stride + 16 * t + 4 * kg] = acc * scale;
   }
