@@ -96,6 +96,22 @@ __device__ __forceinline__ f32x16 vs_block_scores(const char* stage, const Frag&
   return acc;
 }
 
+// S of one 32-key block for this wave's 32 query rows (queries as the A
+// operand): lane l gets key l % 32 for rows 8 (v / 4) + 4 (l / 32) + v % 4.
+__device__ __forceinline__ f32x16 vs_block_rows(const char* stage, const Frag& f) {
+  const int l = threadIdx.x & 63, qn = l & 31, hh = l >> 5;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  u32x4 kf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const u32x4*)(stage + qn * 256 + vs_swz(qn, 2 * ks + hh) * 16);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.q[ks], __builtin_bit_cast(bf16x8, kf[ks]), acc, 0, 0, 0);
+  return acc;
+}
+
 struct VsGroupInfo {
   int ng, hi, h, kvh;                // heads in the group, this wave's listed index and head, KV head
   bool on;                           // this wave's head slot is used
@@ -122,7 +138,7 @@ __device__ __forceinline__ void vs_wait_vm_upto(int n) {
 }
 
 constexpr int P1ST = 6;              // pass 1 ring stages: blocks prefetched five ahead
-constexpr int P2ST = 3;              // pass 2 ring stages: blocks prefetched two ahead
+constexpr int P2ST = 4;              // pass 2 ring stages: blocks prefetched three ahead
 
 __global__ __launch_bounds__(GT) void vs_group_pass1_kernel(VsScoreArgs a, VsGroupTable t) {
   __shared__ __align__(1024) char s_k[P1ST][KB * 256];
@@ -225,21 +241,30 @@ __global__ __launch_bounds__(1024) void vs_row_stats_kernel(VsScoreArgs a) {
   }
 }
 
-// Pass 2.  The loop issues no global stores (a store shares the DMA's counter
-// and would make the partial waits unsafe): a chunk's column sums and diagonal
-// partials collect in LDS and are written out once at the end.
-__global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGroupTable t) {
+// Pass 2.  Per block a wave forms S (its 32 query rows by the block's 32 keys)
+// with the query fragments as the A operand, so lane l holds key l % 32 of the
+// block for sixteen rows.  Column sums are the lane's own sixteen weights plus
+// those of lane l ^ 32 (the other sixteen rows).  Diagonal sums: for each of
+// the sixteen rows rl, lane t takes the weight of key (rl - t) mod 32 from its
+// half of the wave (ds_bpermute), which lies on diagonal rl - key = t when
+// t <= rl and t - 32 otherwise; the two accumulators of lane t are offsets
+// base + t and base + t - 32 of the block, and the second is the first one of
+// the next block, so it is carried and added there.  Sums run in a fixed order
+// (rows ascending within a half, then the halves, then block before carry,
+// then rows 0-31 before 32-63).  The loop issues no global stores (a store
+// shares the DMA's counter and would make the partial waits unsafe): each
+// wave's column sums and diagonal partials collect in its own LDS rows and
+// are written out once at the end.
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(4))) void vs_group_pass2_kernel(VsScoreArgs a, VsGroupTable t) {
   __shared__ __align__(1024) char s_k[P2ST][KB * 256];
-  __shared__ float s_p[GH][64 * (KB + 1)];
-  __shared__ float s_diag[GH][kVsChunkMax + 64];
-  __shared__ float s_col[GH][kVsChunkMax];
+  __shared__ float s_dw[2 * GH][kVsChunkMax + 64];
+  __shared__ float s_cw[2 * GH][kVsChunkMax];
   __shared__ float s_mr[GH][64], s_il[GH][64];
   const int CK = a.chunk_keys, c = blockIdx.y, b = blockIdx.z;
   const VsGroupInfo gi = vs_group_info(a, t);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hh = l >> 5, qn = l & 31;
   const int g = w >> 1;
-  const int r = 32 * (w & 1) + qn;
-  const int pr = a.Nk - a.last_q + r;
+  const int r = 32 * (w & 1) + qn;           // the query row this lane loads
   const size_t row = (size_t)(b * a.heads.n + gi.hi);
 
   // each row's final maximum and 1 / sum (vs_row_stats_kernel)
@@ -247,71 +272,84 @@ __global__ __launch_bounds__(GT) void vs_group_pass2_kernel(VsScoreArgs a, VsGro
     s_mr[g][l] = a.row_stats[row * 128 + l];
     s_il[g][l] = a.row_stats[row * 128 + 64 + l];
   }
-  for (int i = tid; i < GH * (kVsChunkMax + 64); i += GT) (&s_diag[0][0])[i] = 0.f;
+  for (int i = tid; i < 2 * GH * (kVsChunkMax + 64); i += GT) (&s_dw[0][0])[i] = 0.f;
   Frag f;
   load_qfrag(a, b, gi.h, gi.on ? r : 64, f);
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + gi.kvh) * a.Nk) * 128;
   const int nblk = (a.Nk + KB - 1) / KB;
   const int kb0 = c * (CK / KB), kb1 = min(nblk, kb0 + CK / KB);
-  const int o_min = a.Nk - a.last_q - (c + 1) * CK + 1;   // offset of diagonal slot 0 of this chunk
-  float* sp = s_p[g];
-  const int tl = tid & 127;                               // this thread's place among its head's 128
-  __syncthreads();                                        // row statistics visible; s_diag cleared
-  const float mr = s_mr[g][r & 63], il = s_il[g][r & 63];
+  __syncthreads();                                        // row statistics visible; s_dw cleared
+  // rows of this lane's sixteen weights: rl(v) = 8 (v / 4) + 4 hh + v % 4, so
+  // the statistics of rows v = 4 j .. 4 j + 3 are four adjacent floats
+  const float* smr = &s_mr[g][32 * (w & 1) + 4 * hh];
+  const float* sil = &s_il[g][32 * (w & 1) + 4 * hh];
+  const int p0 = a.Nk - a.last_q + 32 * (w & 1);          // position of the wave's row 0
+  const int rows_on = a.last_q - 32 * (w & 1);            // rows rl < rows_on exist
+  float* dw = s_dw[w];
+  float* cw = s_cw[w];
+  // slot of offset base(kb) + qn, base(kb) = p0 - 32 kb, with slot 0 at offset
+  // Nk - last_q - (c + 1) CK + 1
+  const int slot0 = 32 * (w & 1) + CK - 1 + qn;
+  float carry = 0.f;
   // from here on the DMAs are the only vector memory operations in flight
   for (int i = 0; i < P2ST - 1 && kb0 + i < kb1; ++i) vs_issue_block(kp, a.Nk, kb0 + i, s_k[i]);
   vs_take_q(f);
   for (int kb = kb0; kb < kb1; ++kb) {
     const int st = (kb - kb0) % P2ST;
     vs_wait_vm_upto(min(P2ST - 2, kb1 - 1 - kb));         // block kb landed (later ones may be in flight)
-    __syncthreads();                                     // ... for every wave; the last block's sums are done
+    __syncthreads();                                     // ... for every wave; all are done with kb - 1
     if (kb + P2ST - 1 < kb1) vs_issue_block(kp, a.Nk, kb + P2ST - 1, s_k[(st + P2ST - 1) % P2ST]);
     if (gi.on) {
-      const f32x16 acc = vs_block_scores(s_k[st], f);
+      const f32x16 acc = vs_block_rows(s_k[st], f);
+      const int key = kb * KB + qn;
+      float p[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // read here rather than kept in registers: a wave's statistics would
+        // take 32 registers for the whole loop
+        const f32x4 mr = *(const f32x4*)(smr + 8 * j), il = *(const f32x4*)(sil + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * j + e, rl = 8 * j + 4 * hh + e;
+          const bool ok = key < a.Nk && key <= p0 + rl && rl < rows_on;
+          p[v] = ok ? __builtin_amdgcn_exp2f(acc[v] * kScale2 - mr[e]) * il[e] : 0.f;
+        }
+      }
+      float cs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cs += p[v];
+      float da = 0.f, db = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int cc = 8 * (v >> 2) + 4 * hh + (v & 3);
-        const int key = kb * KB + cc;
-        const bool ok = key < a.Nk && key <= pr && r < a.last_q;
-        sp[r * (KB + 1) + cc] = ok ? __builtin_amdgcn_exp2f(acc[v] * kScale2 - mr) * il : 0.f;
+        const int rl = 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int src = (((rl - qn) & 31) + 32 * hh) << 2;
+        const float x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, p[v])));
+        const bool lo = qn <= rl;
+        da += lo ? x : 0.f;
+        db += lo ? 0.f : x;
       }
-    }
-    __syncthreads();
-    if (gi.on) {
-      {
-        // column sums: four lanes per column, 16 rows each, then (p0 + p1) + (p2 + p3)
-        const int col = tl >> 2, part = tl & 3;
-        float cs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) cs += sp[(16 * part + i) * (KB + 1) + col];
-        cs += __shfl_xor(cs, 1, 64);
-        cs += __shfl_xor(cs, 2, 64);
-        if (part == 0) s_col[g][(kb - kb0) * KB + col] = cs;
-      }
-      if (tl < 95) {
-        // diagonal dl = r - cc in [-31, 63]: the terms of keys cc = 0 .. 31 (rows
-        // dl + cc, ascending); a fixed count lets eight reads be in flight at a
-        // time.  Rows outside [0, 63] read row 0 (in bounds) and add nothing.
-        const int dl = tl - 31;
-        float ds = 0.f;
-#pragma unroll 8
-        for (int cc = 0; cc < KB; ++cc) {
-          const int rr = dl + cc;
-          const bool in = rr >= 0 && rr < 64;
-          const float x = sp[(in ? rr : 0) * (KB + 1) + cc];
-          ds += in ? x : 0.f;
-        }
-        s_diag[g][a.Nk - a.last_q - kb * KB + dl - o_min] += ds;
+      const float cs2 = __shfl_xor(cs, 32, 64);
+      const float da2 = __shfl_xor(da, 32, 64);
+      const float db2 = __shfl_xor(db, 32, 64);
+      if (hh == 0) {
+        const int i = kb - kb0;
+        cw[i * KB + qn] = cs + cs2;
+        dw[slot0 - KB * i] = (da + da2) + carry;
+        carry = db + db2;
       }
     }
   }
+  // the last block's carried offsets (lane 0's is always zero: no key lies
+  // 32 positions after its row within a block)
+  if (gi.on && hh == 0 && qn > 0) dw[slot0 - KB * (kb1 - kb0)] = carry;
   __syncthreads();
   if (gi.on) {
+    const int tl = tid & 127;
     float* vo = a.v_out + row * a.Nk;
     const int n = min(a.Nk, kb1 * KB) - kb0 * KB;
-    for (int i = tl; i < n; i += 128) vo[kb0 * KB + i] = s_col[g][i];
+    for (int i = tl; i < n; i += 128) vo[kb0 * KB + i] = s_cw[2 * g][i] + s_cw[2 * g + 1][i];
     float* pd = a.part_diag + (row * a.nchunks + c) * (size_t)(CK + 64);
-    for (int i = tl; i < CK + 64; i += 128) pd[i] = s_diag[g][i];
+    for (int i = tl; i < CK + 64; i += 128) pd[i] = s_dw[2 * g][i] + s_dw[2 * g + 1][i];
   }
 }
 
