@@ -515,6 +515,12 @@ constexpr int kSmallUnits = 7168;                  // 32-key units per item (key
 constexpr int OFF_UMASK = 2 * SLOT;
 constexpr int OFF_ULIST = OFF_UMASK + kSmallUnits * 2;
 static_assert(OFF_ULIST + kSmallUnits * 4 <= OFF_MISC, "small-block regions overlap the shared counters");
+// Blocks of 16 gathered in pairs: behind the same two-slot ring, one mask byte
+// per 16-key block and the compacted block list.
+constexpr int kPairBlocks = 8192;                  // 16-key blocks per item (keys < 131072)
+constexpr int OFF_BMASK = 2 * SLOT;
+constexpr int OFF_BLIST = OFF_BMASK + kPairBlocks;
+static_assert(OFF_BLIST + kPairBlocks * 4 <= OFF_MISC, "paired-block regions overlap the shared counters");
 
 // Ring slot arithmetic on small non-negative values (unsigned: a multiply-high
 // and a shift, not the signed remainder's fix-ups).
@@ -890,6 +896,84 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAV
           }
         }
         __syncthreads();                         // the slots are free for the gather phase
+      } else if (SMALL && it.kind == 2 && a.block == 16 && it.last_pos / 16 < kPairBlocks) {
+        // Blocks of 16, gathered per item in pairs: the item's eight query
+        // blocks mark every 16-key block they selected (bit q for query block
+        // q), the marked blocks are compacted into one ascending list, and
+        // each two consecutive list entries, adjacent in key space or not, fill
+        // one 32-key unit of the ring (keys 0-15 from the first, 16-31 from the
+        // second).  Query blocks of an item mostly select the same blocks, so
+        // a unit is mostly full for both query blocks of a wave, where a
+        // 32-key unit of key space would often carry one selected half.
+        __syncthreads();                         // every wave has read the item number; the arena is free
+        const int nb = it.last_pos / 16 + 1;     // 16-key blocks the item's rows can see
+        uint8_t* const bmask = (uint8_t*)(s_lds + OFF_BMASK);
+        uint32_t* const bmask32 = (uint32_t*)bmask;
+        uint32_t* const blist = (uint32_t*)(s_lds + OFF_BLIST);
+        for (int i = tid; i < (nb + 3) / 4; i += NT) bmask32[i] = 0u;
+        __syncthreads();
+        {
+          const int I0 = it.P0 / 16;
+          for (int q = w; q < 8; q += 4) {
+            const int I = I0 + q;                // absolute query block
+            const int Ir = I - a.qb0;            // its row of the chunk's lists
+            if (Ir >= a.nqb || I * 16 > it.last_pos) continue;
+            const int32_t* li = a.bidx + ((size_t)it.bh * a.nqb + Ir) * a.bcap;
+            const int n = min(ldc(a.bcount, (size_t)it.bh * a.nqb + Ir), a.bcap);
+            for (int x = l; x < n; x += 64) {
+              const int J = li[x];
+              if (J < 0 || J >= nb) continue;   // out of range, or after the item's last row
+              atomicOr(&bmask32[J >> 2], (1u << q) << (8 * (J & 3)));
+            }
+          }
+        }
+        __syncthreads();
+        int nlist = 0;
+        for (int j0 = 0; j0 < nb; j0 += NT) {
+          const int J = j0 + tid;
+          const uint32_t m = J < nb ? (uint32_t)bmask[J] : 0u;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(m != 0u);
+          if (l == 0) s_misc[1 + w] = __popcll(bal);
+          __syncthreads();
+          int off = nlist;
+          for (int i = 0; i < w; ++i) off += s_misc[1 + i];
+          if (m != 0u) blist[off + ballot_rank(bal)] = (uint32_t)J | (m << 16);
+          nlist += s_misc[1] + s_misc[2] + s_misc[3] + s_misc[4];
+          __syncthreads();
+        }
+        // one unit from two blocks: rows 16 j + rl of the slot from block Jj
+        auto issue_pair = [&](int J0, int J1, uint32_t lb) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int r = 16 * j + rl;
+            const int key = min(16 * (j ? J1 : J0) + rl, a.Nk - 1);
+            dma16(kbp + (size_t)key * 128 + swz_k(r, l & 15) * 8, lb + (4 * j + w) * 1024);
+            dma16(vbp + (size_t)key * 128 + swz_v(r, l & 15) * 8, lb + 8192 + (4 * j + w) * 1024);
+          }
+        };
+        // entry 2 i + 1 of an odd list is absent: block 0, no query block
+        auto entry = [&](int x) { return x < nlist ? blist[x] : 0u; };
+        const int npair = (nlist + 1) / 2;
+        if (npair > 0) issue_pair((int)(entry(0) & 0xFFFFu), (int)(entry(1) & 0xFFFFu), ring);
+        take_q();
+        const int qb = (32 * w + qn) / 16;       // this lane's query block within the item
+        auto causal16 = [](int top) -> uint32_t {   // bits c <= top of 16
+          return top < 0 ? 0u : top >= 15 ? 0xFFFFu : (2u << top) - 1u;
+        };
+        for (int i = 0; i < npair; ++i) {
+          const uint32_t e0 = entry(2 * i), e1 = entry(2 * i + 1);
+          wait_vm();
+          __syncthreads();                       // unit i landed; every wave is done with unit i - 1
+          if (i + 1 < npair)
+            issue_pair((int)(entry(2 * i + 2) & 0xFFFFu), (int)(entry(2 * i + 3) & 0xFFFFu),
+                       ring + (uint32_t)(((i + 1) & 1) * SLOT));
+          const int J0 = (int)(e0 & 0xFFFFu), J1 = (int)(e1 & 0xFFFFu);
+          uint32_t M = (((e0 >> (16 + qb)) & 1u) ? causal16(iq - 16 * J0) : 0u) |
+                       ((((e1 >> (16 + qb)) & 1u) ? causal16(iq - 16 * J1) : 0u) << 16);
+          const uint32_t st = (uint32_t)((i & 1) * SLOT);
+          sub32(st, st + 8192, M);
+        }
+        it.kind = 4;                             // no tile steps for this item
       } else if (SMALL && it.kind == 2 && a.block < TK && it.last_pos / 32 < kSmallUnits) {
         // Blocks of 16 or 32, gathered per item: the item's query blocks (8 of
         // 16 rows or 4 of 32) mark the 16-key halves of every 32-key unit they
