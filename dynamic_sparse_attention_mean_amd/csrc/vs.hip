@@ -51,10 +51,11 @@ constexpr float kScale2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(
 // The two passes per KV group: a workgroup takes up to GH listed heads that
 // read the same KV head (two waves per head: query rows 0-31 and 32-63), so
 // each 32-key block of K is brought into LDS once (DMA) for all of them.
-// Per block a wave forms S^T for its 32 rows on v_mfma_f32_32x32x16_bf16 with
-// the K fragments read from LDS.  Pass 2 stages each head's weights in LDS and
-// reduces them along columns (four lanes per column, rows in a fixed order)
-// and diagonals (one lane per diagonal, rows ascending).
+// Per block a wave forms the scores of its 32 rows on v_mfma_f32_32x32x16_bf16
+// with the K fragments read from LDS: pass 1 as S^T (a lane holds one row, so
+// row maxima and sums stay in the lane), pass 2 as S (a lane holds one key
+// column, so column sums stay in registers and diagonal sums take a lane
+// rotation, as described at the kernel).
 constexpr int GH = 4;                // heads per workgroup
 constexpr int GT = 2 * GH * 64;      // threads: wave w serves head slot w / 2, rows 32 (w % 2) ..
 constexpr int KB = 32;               // keys per block

@@ -349,3 +349,17 @@ def test_block_sweep_32k_small_blocks(block):
     os_ = osets_of(w, heads)
     check_sets(w, layer, heads, os_)
     check_rows(w, layer, o, lse, heads, os_, rows_per_head=24, o32=o32)
+
+
+def test_block16_past_paired_limit():
+    """Blocks of 16 on a sequence whose items see more than 8192 16-key blocks
+    (N=135168): the items near the end take the 32-key unit gather, the
+    earlier ones the paired gather; selections against the oracle within the
+    band, sampled rows (the last ones included) against the oracle's
+    attention over its own sets."""
+    w = synth.token_planted(block=16, N=135168, H=2)
+    layer, o, lse, o32 = run_layer(w)
+    heads = [0, 1]
+    os_ = osets_of(w, heads)
+    check_sets(w, layer, heads, os_)
+    check_rows(w, layer, o, lse, heads, os_, rows_per_head=24, o32=o32)
